@@ -1,0 +1,9 @@
+"""fp64 CPU oracle of the focused block-diffusion step (score -> select -> compact -> attend).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the bench's CPU-baseline leg,
+never by the product path.  It shares no code with the HIP library.
+"""
+from .focus_oracle import (  # noqa: F401
+    adaptive_threshold, bf16_to_f64, compact, kth_boundary, layer_importance, ragged_paged_attn,
+    request_budget, request_kv, score_l01, select_budget, step, to_f64,
+)
