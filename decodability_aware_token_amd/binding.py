@@ -1,0 +1,191 @@
+"""Thin Python binding of libfocus.so (the C ABI in include/focus.h).
+
+Argument marshalling only: shapes are read from torch tensors, outputs and workspaces are
+allocated with torch on the tensors' device, and every call goes straight to the library on the
+current HIP stream.  No step of the computation runs here.  If the library has not been built,
+importing this module raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfocus.so")
+
+FOCUS_OK = 0
+FOCUS_ERR_INVALID_ARG = -1
+FOCUS_ERR_UNSUPPORTED = -2
+FOCUS_ERR_WORKSPACE = -3
+FOCUS_ERR_HIP = -4
+FOCUS_F32 = 0
+FOCUS_BF16 = 1
+
+_c_void_p, _c_int, _c_float, _c_size_t = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_c_int64 = ctypes.c_int64
+
+# name -> (restype, argtypes), mirroring include/focus.h
+SIGNATURES = {
+    "focus_status_string": (ctypes.c_char_p, [_c_int]),
+    "focus_version": (_c_int, []),
+    "focus_score_l01_workspace_size": (_c_size_t, [_c_int] * 5),
+    "focus_score_l01": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p,
+                                                                  _c_size_t, _c_void_p]),
+    "focus_select_budget": (_c_int, [_c_void_p] * 3 + [_c_int, _c_float, _c_int, _c_int, _c_int,
+                                                       _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "focus_compact": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int64, _c_int, _c_void_p,
+                               _c_void_p, _c_void_p, _c_void_p]),
+    "focus_ragged_paged_attn_workspace_size": (_c_size_t, [_c_int] * 8),
+    "focus_ragged_paged_attn": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                         _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                         _c_void_p] + [_c_int] * 7 + [_c_float, _c_void_p,
+                                                                      _c_void_p, _c_void_p,
+                                                                      _c_size_t, _c_void_p]),
+}
+
+
+class FocusError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)} ({code})")
+        self.code = code
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "or `python -m decodability_aware_token_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(code: int) -> str:
+    return lib().focus_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int):
+    if code != FOCUS_OK:
+        raise FocusError(fn, code)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors handed to libfocus must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[Optional[torch.Tensor], int]:
+    if nbytes == 0:
+        return ws, 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ------------------------------------------------------------------------------------------
+def score_l01(q0, k0, q1, k1, sm_scale: float, delta=None, workspace=None) -> torch.Tensor:
+    """delta [B, blk] f32 = layer-1 minus layer-0 importance (see focus_score_l01)."""
+    B, blk, Hq, d = q0.shape
+    Hkv = k0.shape[2]
+    dt = {torch.float32: FOCUS_F32, torch.bfloat16: FOCUS_BF16}[q0.dtype]
+    if delta is None:
+        delta = torch.empty((B, blk), dtype=torch.float32, device=q0.device)
+    need = lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
+    workspace, wsb = _workspace(need, q0.device, workspace)
+    rc = lib().focus_score_l01(_ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), dt, B, blk, Hq, Hkv, d,
+                               float(sm_scale), _ptr(delta), _ptr(workspace), wsb,
+                               _stream(q0.device))
+    _check("focus_score_l01", rc)
+    return delta
+
+
+def select_budget(delta, masked, budget=None, adaptive=None, keep=None, kept_count=None):
+    """keep [B, blk] u8, kept_count [B] i32 (see focus_select_budget).
+
+    ``adaptive`` is None (use ``budget``) or a tuple (beta, lo, hi)."""
+    B, blk = delta.shape
+    if keep is None:
+        keep = torch.empty((B, blk), dtype=torch.uint8, device=delta.device)
+    if kept_count is None:
+        kept_count = torch.empty(B, dtype=torch.int32, device=delta.device)
+    beta, lo, hi = adaptive if adaptive is not None else (0.0, 0, 0)
+    rc = lib().focus_select_budget(_ptr(delta), _ptr(masked), _ptr(budget),
+                                   1 if adaptive is not None else 0, float(beta), int(lo), int(hi),
+                                   B, blk, _ptr(keep), _ptr(kept_count), _stream(delta.device))
+    _check("focus_select_budget", rc)
+    return keep, kept_count
+
+
+def compact(keep, rows=None, cap: Optional[int] = None, offsets=None, kept_pos=None,
+            gathered=None, with_pos: bool = True):
+    """offsets [B+1], kept_pos [cap], gathered [cap, *row] (see focus_compact)."""
+    B, blk = keep.shape
+    dev = keep.device
+    if cap is None:
+        cap = B * blk
+    if offsets is None:
+        offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if kept_pos is None and with_pos:
+        kept_pos = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    row_bytes = 0
+    if rows is not None:
+        row_shape = rows.shape[2:]
+        row_bytes = rows[0, 0].numel() * rows.element_size()
+        if gathered is None:
+            gathered = torch.empty((max(cap, 1),) + tuple(row_shape), dtype=rows.dtype, device=dev)
+    rc = lib().focus_compact(_ptr(keep), B, blk, _ptr(rows), row_bytes, int(cap), _ptr(offsets),
+                             _ptr(kept_pos), _ptr(gathered), _stream(dev))
+    _check("focus_compact", rc)
+    return offsets, kept_pos, gathered
+
+
+def attn_workspace_bytes(B, blk, Hq, Hkv, d, S, max_pages, max_kept) -> int:
+    return int(lib().focus_ragged_paged_attn_workspace_size(B, blk, Hq, Hkv, d, S, max_pages,
+                                                            max_kept))
+
+
+def ragged_paged_attn(q, offsets, k_cache, v_cache, page_table, prefix_len, k_blk, v_blk,
+                      max_kept: int, sm_scale: float, out=None, lse=None, want_lse=True,
+                      workspace=None):
+    """out [cap, Hq, d] bf16, lse [cap, Hq] f32 (see focus_ragged_paged_attn).
+
+    q [cap, Hq, d]; k_cache [pages, Hkv, d/8, S, 8]; v_cache [pages, Hkv, S/8, d, 8];
+    k_blk [B, Hkv, d/8, blk, 8]; v_blk [B, Hkv, blk/8, d, 8]; page_table [B, max_pages]."""
+    cap, Hq, d = q.shape
+    num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
+    S = k_cache.shape[3]
+    B, max_pages = page_table.shape
+    blk = k_blk.shape[3]
+    dev = q.device
+    if out is None:
+        out = torch.empty((cap, Hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((cap, Hq), dtype=torch.float32, device=dev)
+    need = attn_workspace_bytes(B, blk, Hq, Hkv, d, S, max_pages, max_kept)
+    workspace, wsb = _workspace(need, dev, workspace)
+    rc = lib().focus_ragged_paged_attn(_ptr(q), _ptr(offsets), cap, _ptr(k_cache), _ptr(v_cache),
+                                       num_pages, _ptr(page_table), max_pages, _ptr(prefix_len),
+                                       _ptr(k_blk), _ptr(v_blk), B, blk, Hq, Hkv, d, S,
+                                       int(max_kept), float(sm_scale), _ptr(out), _ptr(lse),
+                                       _ptr(workspace), wsb, _stream(dev))
+    _check("focus_ragged_paged_attn", rc)
+    return out, lse

@@ -1,0 +1,190 @@
+// C ABI of the focused block-diffusion step (declared in include/focus.h): validates every
+// argument on the host, sizes the launch and hands over to the kernels' launchers.  Nothing
+// here allocates memory or synchronises the host.
+#include "focus.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxB = 4096;
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool group_ok(int Hq, int Hkv) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return false;
+  const int G = Hq / Hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+int status_of(hipError_t e) { return e == hipSuccess ? FOCUS_OK : FOCUS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* focus_status_string(int code) {
+  switch (code) {
+    case FOCUS_OK: return "ok";
+    case FOCUS_ERR_INVALID_ARG: return "invalid argument";
+    case FOCUS_ERR_UNSUPPORTED: return "unsupported size";
+    case FOCUS_ERR_WORKSPACE: return "workspace missing or too small";
+    case FOCUS_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int focus_version(void) { return kVersion; }
+
+size_t focus_score_l01_workspace_size(int B, int blk, int Hq, int Hkv, int d) {
+  (void)Hq;
+  (void)d;
+  if (B <= 0 || blk <= 0 || Hkv <= 0) return 0;
+  return focus::score_workspace_bytes(B, blk, Hkv);
+}
+
+int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* k1, int dtype,
+                    int B, int blk, int Hq, int Hkv, int d, float sm_scale, float* delta,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q0 || !k0 || !q1 || !k1 || !delta) return FOCUS_ERR_INVALID_ARG;
+  if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FOCUS_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return FOCUS_ERR_INVALID_ARG;
+  if (dtype != FOCUS_F32 && dtype != FOCUS_BF16) return FOCUS_ERR_UNSUPPORTED;
+  if (Hq % Hkv != 0) return FOCUS_ERR_INVALID_ARG;
+  if (!group_ok(Hq, Hkv) || Hkv > 64) return FOCUS_ERR_UNSUPPORTED;
+  if (!pow2_in(blk, 16, 64) || (d != 64 && d != 128) || B > kMaxB) return FOCUS_ERR_UNSUPPORTED;
+  if (!aligned16(q0) || !aligned16(k0) || !aligned16(q1) || !aligned16(k1))
+    return FOCUS_ERR_INVALID_ARG;
+  const size_t need = focus::score_workspace_bytes(B, blk, Hkv);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FOCUS_ERR_WORKSPACE;
+  focus::ScoreArgs a{};
+  a.q0 = q0;
+  a.k0 = k0;
+  a.q1 = q1;
+  a.k1 = k1;
+  a.is_bf16 = dtype == FOCUS_BF16;
+  a.B = B;
+  a.blk = blk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.delta = delta;
+  a.part = static_cast<float*>(workspace);
+  return status_of(focus::launch_score(a, stream));
+}
+
+int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t* budget,
+                        int adaptive, float beta, int lo, int hi, int B, int blk, uint8_t* keep,
+                        int32_t* kept_count, hipStream_t stream) {
+  if (!delta || !masked || !keep || !kept_count) return FOCUS_ERR_INVALID_ARG;
+  if (!adaptive && !budget) return FOCUS_ERR_INVALID_ARG;
+  if (B <= 0 || blk <= 0) return FOCUS_ERR_INVALID_ARG;
+  if (adaptive && (!std::isfinite(beta) || lo > hi)) return FOCUS_ERR_INVALID_ARG;
+  if (!pow2_in(blk, 16, 64) || B > kMaxB) return FOCUS_ERR_UNSUPPORTED;
+  focus::SelectArgs a{};
+  a.delta = delta;
+  a.masked = masked;
+  a.budget = budget;
+  a.adaptive = adaptive ? 1 : 0;
+  a.beta = beta;
+  a.lo = lo;
+  a.hi = hi;
+  a.B = B;
+  a.blk = blk;
+  a.keep = keep;
+  a.kept_count = kept_count;
+  return status_of(focus::launch_select(a, stream));
+}
+
+int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
+                  int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,
+                  hipStream_t stream) {
+  if (!keep || !offsets) return FOCUS_ERR_INVALID_ARG;
+  if (B <= 0 || blk <= 0 || cap < 0) return FOCUS_ERR_INVALID_ARG;
+  if ((rows == nullptr) != (gathered == nullptr)) return FOCUS_ERR_INVALID_ARG;
+  if (!aligned4(keep)) return FOCUS_ERR_INVALID_ARG;
+  if (!pow2_in(blk, 16, 64) || B > kMaxB) return FOCUS_ERR_UNSUPPORTED;
+  if (rows) {
+    if (row_bytes <= 0) return FOCUS_ERR_INVALID_ARG;
+    if (row_bytes % 16 != 0 || !aligned16(rows) || !aligned16(gathered))
+      return FOCUS_ERR_UNSUPPORTED;
+  }
+  focus::CompactArgs a{};
+  a.keep = keep;
+  a.B = B;
+  a.blk = blk;
+  a.rows = rows;
+  a.row_bytes = rows ? row_bytes : 0;
+  a.cap = cap;
+  a.offsets = offsets;
+  a.kept_pos = kept_pos;
+  a.gathered = gathered;
+  return status_of(focus::launch_compact(a, stream));
+}
+
+size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, int d, int S,
+                                              int max_pages, int max_kept) {
+  if (B <= 0 || blk <= 0 || !group_ok(Hq, Hkv) || d <= 0 || S <= 0 || max_pages < 0 ||
+      max_kept <= 0)
+    return 0;
+  return focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept).ws_bytes;
+}
+
+int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, const void* k_cache,
+                            const void* v_cache, int num_pages, const int32_t* page_table,
+                            int max_pages, const int32_t* prefix_len, const void* k_blk,
+                            const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
+                            int max_kept, float sm_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !offsets || !prefix_len || !k_blk || !v_blk || !out) return FOCUS_ERR_INVALID_ARG;
+  if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || S <= 0 || cap < 0 ||
+      num_pages < 0 || max_pages < 0 || max_kept <= 0)
+    return FOCUS_ERR_INVALID_ARG;
+  if (max_pages > 0 && (!k_cache || !v_cache || !page_table || num_pages <= 0))
+    return FOCUS_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return FOCUS_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0 || max_kept > blk) return FOCUS_ERR_INVALID_ARG;
+  if (!group_ok(Hq, Hkv) || Hkv > 64) return FOCUS_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || !pow2_in(S, 16, 64) || !pow2_in(blk, 16, 64) || B > kMaxB)
+    return FOCUS_ERR_UNSUPPORTED;
+  if ((long long)max_pages * S > (1LL << 24)) return FOCUS_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
+      (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)))
+    return FOCUS_ERR_INVALID_ARG;
+  const focus::AttnPlan plan = focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return FOCUS_ERR_WORKSPACE;
+  if (cap == 0) return FOCUS_OK;
+  focus::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.offsets = offsets;
+  a.cap = cap;
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.num_pages = num_pages;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.prefix_len = prefix_len;
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.B = B;
+  a.blk = blk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.S = S;
+  a.max_kept = max_kept;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.workspace = workspace;
+  return status_of(focus::launch_attn(a, plan, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Host-side launchers of the gfx950 kernels (one per .hip file); called by the C ABI after it
+// has validated every argument.  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace focus {
+
+struct ScoreArgs {
+  const void* q0;
+  const void* k0;
+  const void* q1;
+  const void* k1;
+  int is_bf16;
+  int B, blk, Hq, Hkv, d;
+  float scale_log2;  // sm_scale * log2(e)
+  float* delta;      // [B, blk]
+  float* part;       // workspace [B, Hkv, blk]
+};
+size_t score_workspace_bytes(int B, int blk, int Hkv);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+
+struct SelectArgs {
+  const float* delta;
+  const uint8_t* masked;
+  const int32_t* budget;
+  int adaptive;
+  float beta;
+  int lo, hi;
+  int B, blk;
+  uint8_t* keep;
+  int32_t* kept_count;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+struct CompactArgs {
+  const uint8_t* keep;
+  int B, blk;
+  const void* rows;
+  int64_t row_bytes;
+  int cap;
+  int32_t* offsets;
+  int32_t* kept_pos;
+  void* gathered;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const int32_t* offsets;
+  int cap;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  int num_pages;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* prefix_len;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  int B, blk, Hq, Hkv, d, S;
+  int max_kept;
+  float scale_log2;
+  uint16_t* out;
+  float* lse;
+  void* workspace;
+};
+struct AttnPlan {
+  int qt;           // 16-row query tiles per work item (1, 2 or 4)
+  int nqg;          // query groups per (request, kv head)
+  int tiles_split;  // 32-key tiles per split (multiple of 4)
+  int nsplit_max;   // splits per (request, kv head) at the longest possible prefix
+  size_t ws_bytes;  // partial-result workspace
+};
+AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept);
+hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
+
+}  // namespace focus

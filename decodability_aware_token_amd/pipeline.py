@@ -1,0 +1,95 @@
+"""One focused block-diffusion step on the GPU: score -> select -> compact (hidden, Q) -> attend.
+
+`FocusStep` preallocates every output and workspace once for a fixed batch shape, then `run()`
+issues the four C-ABI calls back to back on the current stream with no host synchronisation:
+ragged sizes stay on the device, and the attention is sized by the host-known bound max_kept.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding as F
+
+
+@dataclass
+class StepInputs:
+    """Device tensors of one step (layouts as in include/focus.h)."""
+    q0: torch.Tensor
+    k0: torch.Tensor
+    q1: torch.Tensor
+    k1: torch.Tensor
+    masked: torch.Tensor          # [B, blk] u8
+    budget: Optional[torch.Tensor]  # [B] i32, or None with `adaptive`
+    adaptive: Optional[tuple]     # (beta, lo, hi) or None
+    max_kept: int
+    q_att: torch.Tensor           # [B, blk, Hq, d] bf16
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    page_table: torch.Tensor
+    prefix_len: torch.Tensor
+    k_blk: torch.Tensor
+    v_blk: torch.Tensor
+    sm_scale: float
+    hidden: Optional[torch.Tensor] = None  # [B, blk, W] bf16
+
+
+class FocusStep:
+    def __init__(self, inp: StepInputs, cap: Optional[int] = None, want_lse: bool = True):
+        B, blk, Hq, d = inp.q_att.shape
+        Hkv = inp.k_blk.shape[1]
+        dev = inp.q_att.device
+        self.inp = inp
+        self.B, self.blk, self.Hq, self.Hkv, self.d = B, blk, Hq, Hkv, d
+        self.cap = B * blk if cap is None else cap
+        self.delta = torch.empty((B, blk), dtype=torch.float32, device=dev)
+        self.keep = torch.empty((B, blk), dtype=torch.uint8, device=dev)
+        self.kept_count = torch.empty(B, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.kept_pos = torch.empty(max(self.cap, 1), dtype=torch.int32, device=dev)
+        self.q_rows = torch.empty((max(self.cap, 1), Hq, d), dtype=torch.bfloat16, device=dev)
+        self.hidden_rows = None
+        if inp.hidden is not None:
+            self.hidden_rows = torch.empty((max(self.cap, 1), inp.hidden.shape[2]),
+                                           dtype=inp.hidden.dtype, device=dev)
+        self.out = torch.empty((max(self.cap, 1), Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((max(self.cap, 1), Hq), dtype=torch.float32, device=dev) \
+            if want_lse else None
+        nsc = F.lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
+        self.ws_score = torch.empty(max(nsc, 1), dtype=torch.uint8, device=dev)
+        S = inp.k_cache.shape[3]
+        nat = F.attn_workspace_bytes(B, blk, Hq, Hkv, d, S, inp.page_table.shape[1], inp.max_kept)
+        self.ws_attn = torch.empty(max(nat, 1), dtype=torch.uint8, device=dev)
+
+    def score(self):
+        i = self.inp
+        F.score_l01(i.q0, i.k0, i.q1, i.k1, i.sm_scale, delta=self.delta, workspace=self.ws_score)
+
+    def select(self):
+        i = self.inp
+        F.select_budget(self.delta, i.masked, i.budget, i.adaptive, keep=self.keep,
+                        kept_count=self.kept_count)
+
+    def compact_hidden(self):
+        if self.inp.hidden is not None:
+            F.compact(self.keep, self.inp.hidden, self.cap, offsets=self.offsets,
+                      kept_pos=self.kept_pos, gathered=self.hidden_rows)
+
+    def compact_q(self):
+        F.compact(self.keep, self.inp.q_att, self.cap, offsets=self.offsets,
+                  kept_pos=self.kept_pos, gathered=self.q_rows)
+
+    def attend(self):
+        i = self.inp
+        F.ragged_paged_attn(self.q_rows, self.offsets, i.k_cache, i.v_cache, i.page_table,
+                            i.prefix_len, i.k_blk, i.v_blk, i.max_kept, i.sm_scale, out=self.out,
+                            lse=self.lse, want_lse=self.lse is not None, workspace=self.ws_attn)
+
+    def run(self):
+        self.score()
+        self.select()
+        self.compact_hidden()
+        self.compact_q()
+        self.attend()

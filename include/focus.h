@@ -1,0 +1,160 @@
+/*
+ * focus.h -- C ABI of the focused block-diffusion step on AMD Instinct MI355X (gfx950).
+ *
+ * The step (FOCUS, "DLLMs Know How to Tame Their Compute Bound", arXiv 2601.23278):
+ *   1. focus_score_l01        importance delta of every block token, layer 1 minus layer 0
+ *   2. focus_select_budget    keep the k_r masked tokens with the largest delta
+ *   3. focus_compact          ragged offsets + kept positions, gather of the kept rows
+ *   4. focus_ragged_paged_attn  kept queries against paged prefix KV plus intra-block KV
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller, unless stated otherwise.
+ *     The library never allocates, frees or retains memory.
+ *   - Every call is asynchronous on `stream` (0 = the default stream). No call synchronises
+ *     the host; ragged sizes (kept counts, offsets, prefix lengths) never leave the device.
+ *   - A negative return value is a host-detected argument error: nothing was launched.
+ *     FOCUS_ERR_HIP reports a launch error from the HIP runtime.
+ *   - bf16 is IEEE bfloat16 stored as 16-bit words; f32 is IEEE binary32.
+ *   - Indices are row-major; shapes are written outermost first.
+ *   - All results are deterministic: reductions run in a fixed order, no float atomics.
+ */
+#ifndef FOCUS_H_
+#define FOCUS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FOCUS_OK = 0,
+  FOCUS_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes          */
+  FOCUS_ERR_UNSUPPORTED = -2, /* a size outside the supported set (listed per call)          */
+  FOCUS_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the *_workspace_size value */
+  FOCUS_ERR_HIP = -4          /* the HIP runtime reported a launch error                       */
+} focus_status;
+
+typedef enum { FOCUS_F32 = 0, FOCUS_BF16 = 1 } focus_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* focus_status_string(int code);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int focus_version(void);
+
+/* --------------------------------------------------------------------------------------------
+ * 1. Importance scoring.
+ *
+ * Defined by the project page (focus-inference.github.io), Overview cards "Design" (importance
+ * from the early layers' Q/K projections) and "Decodability Signal" (the layer-0 to layer-1
+ * change of importance separates decodable tokens), and by the paper's abstract (importance is
+ * attention-derived).  For request r, layer l in {0,1}, query head h (kv head g = h / (Hq/Hkv)):
+ *     P = softmax_j( sm_scale * q_l[r,i,h,:] . k_l[r,j,g,:] )     (over the blk block keys j)
+ *     I_l[r,j] = sum_h sum_i P[i,j]
+ *     delta[r,j] = I_1[r,j] - I_0[r,j]                              (every position j)
+ *
+ *   q0, q1      [B, blk, Hq, d]   layer-0 / layer-1 block queries, dtype `dtype`
+ *   k0, k1      [B, blk, Hkv, d]  layer-0 / layer-1 block keys,    dtype `dtype`
+ *   dtype       FOCUS_F32 or FOCUS_BF16 (products accumulate in f32)
+ *   delta       [B, blk] f32 output
+ *   workspace   device scratch of at least focus_score_l01_workspace_size(...) bytes
+ *               (may be NULL when that size is 0); contents need no initialisation
+ * Supported: blk in {16,32,64}; d in {64,128}; Hq % Hkv == 0; Hq/Hkv in {1,2,4,8};
+ *            1 <= B <= 65535; Hkv <= 64.  Pointers must be 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+size_t focus_score_l01_workspace_size(int B, int blk, int Hq, int Hkv, int d);
+int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* k1, int dtype,
+                    int B, int blk, int Hq, int Hkv, int d, float sm_scale, float* delta,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
+ * 2. Budgeted selection (target token selection).
+ *
+ * Defined by the project page, cards "Design" (keep likely-decodable candidates under an
+ * adaptive budget) and "Runtime Action" (dynamic budgeting, token eviction), and by the AI
+ * Engineering Academy article's "Arquitetura do FOCUS" section (target token selection).
+ * Candidates of request r are its masked positions (masked[r,j] != 0); m_r is their number.
+ *   adaptive == 0:  b_r = budget[r]
+ *   adaptive != 0:  over the candidates, mu = mean(delta), sigma = population std (both f32),
+ *                   c = #{delta > mu + beta*sigma}, b_r = min(max(c, lo), hi)
+ *   k_r = min(max(b_r, 0), m_r); the k_r candidates with the largest delta are kept, equal
+ *   deltas ordered by lower position first.  Decoded positions are never kept.
+ *
+ *   delta       [B, blk] f32         masked [B, blk] u8      budget [B] i32 (ignored if adaptive)
+ *   keep        [B, blk] u8 output (1 = kept)                kept_count [B] i32 output
+ * Supported: blk in {16,32,64}; 1 <= B <= 2^24.
+ * ------------------------------------------------------------------------------------------ */
+int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t* budget,
+                        int adaptive, float beta, int lo, int hi, int B, int blk, uint8_t* keep,
+                        int32_t* kept_count, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
+ * 3. Compaction + gather (state compaction, ragged execution).
+ *
+ * Defined by the AI Engineering Academy article's "Arquitetura do FOCUS" section (the state is
+ * compacted and evicted tokens dropped) and the project page's "Runtime Action" card (ragged
+ * execution over the kept tokens).
+ *   offsets[0] = 0, offsets[r+1] = offsets[r] + #{j : keep[r,j] != 0}     (offsets[B] = T)
+ *   kept_pos[offsets[r] + t] = t-th kept position of request r, ascending
+ *   gathered[n, :] = rows[r, kept_pos[n], :]   (byte copy of row_bytes bytes)
+ * Entries n >= cap of kept_pos / gathered are not written; offsets always holds the true totals,
+ * so offsets[B] > cap reveals an overflow after the caller synchronises.  cap >= B*blk always
+ * suffices.
+ *
+ *   keep        [B, blk] u8
+ *   rows        [B, blk, row_bytes] bytes, or NULL (then gathered must be NULL: offsets only)
+ *   offsets     [B+1] i32 output        kept_pos [cap] i32 output (may be NULL)
+ *   gathered    [cap, row_bytes] output, or NULL
+ * Supported: blk in {16,32,64}; 1 <= B <= 2^20; row_bytes > 0 and a multiple of 16; rows and
+ *            gathered 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
+                  int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,
+                  hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
+ * 4. Ragged paged attention of the kept queries.
+ *
+ * Defined by the AI Engineering Academy article (ragged paged attention integrated with the
+ * KV-cache management) and the project page's "Runtime Action" (ragged execution, intra-block
+ * KV caching) and "Motivation" (block diffusion: earlier blocks exactly KV-cached, the block is
+ * recomputed bidirectionally) cards.  Row n with offsets[r] <= n < offsets[r+1] is a kept token
+ * of request r.  For each such row and query head h (kv head g = h / (Hq/Hkv)) the keys are the
+ * request's prefix_len[r] cached tokens followed by all blk block tokens (no mask):
+ *   z_t = sm_scale * q[n,h,:] . K_t,   lse[n,h] = log sum_t exp(z_t),
+ *   out[n,h,:] = sum_t exp(z_t - lse[n,h]) V_t        (bf16 in, f32 accumulate, bf16 out)
+ *
+ * Layouts (bf16).  A page holds S consecutive tokens of one request for all kv heads:
+ *   k_cache [num_pages, Hkv, d/8, S, 8]  key (page p, slot s, dim c) at [p, g, c/8, s, c%8]
+ *   v_cache [num_pages, Hkv, S/8, d, 8]  value (p, s, c) at [p, g, s/8, c, s%8]
+ *   k_blk   [B, Hkv, d/8, blk, 8], v_blk [B, Hkv, blk/8, d, 8]: the block KV, same layouts
+ *   page_table [B, max_pages] i32: prefix token t of request r is in page page_table[r, t/S]
+ *   prefix_len [B] i32
+ *   q   [cap, Hq, d] bf16 (compacted queries)   out [cap, Hq, d] bf16   lse [cap, Hq] f32 or NULL
+ * max_kept is an upper bound of every kept count (offsets[r+1]-offsets[r]); it sizes the
+ * launch.  Rows t >= max_kept of a request are not written.  Rows n >= cap are not read or
+ * written.  Device data the host cannot check: a request whose prefix_len is negative or above
+ * max_pages*S, or whose used page ids fall outside [0, num_pages), gets NaN in all its output
+ * rows instead of a memory access.
+ *   workspace   at least focus_ragged_paged_attn_workspace_size(...) bytes, no initialisation
+ * Supported: d in {64,128}; S in {16,32,64}; blk in {16,32,64}; Hq/Hkv in {1,2,4,8};
+ *            1 <= max_kept <= blk; 1 <= B <= 65535; pointers 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, int d, int S,
+                                              int max_pages, int max_kept);
+int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, const void* k_cache,
+                            const void* v_cache, int num_pages, const int32_t* page_table,
+                            int max_pages, const int32_t* prefix_len, const void* k_blk,
+                            const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
+                            int max_kept, float sm_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOCUS_H_ */

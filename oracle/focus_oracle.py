@@ -64,7 +64,7 @@ def layer_importance(q: np.ndarray, k: np.ndarray, sm_scale: float) -> np.ndarra
     imp = np.zeros((B, blk), dtype=np.float64)
     for h in range(Hq):
         g = h // G
-        s = sm_scale * np.einsum("bid,bjd->bij", q[:, :, h, :], k[:, :, g, :])  # [B, i, j]
+        s = sm_scale * (q[:, :, h, :] @ k[:, :, g, :].transpose(0, 2, 1))    # [B, i, j]
         s = s - s.max(axis=2, keepdims=True)
         p = np.exp(s)
         p = p / p.sum(axis=2, keepdims=True)       # row softmax over the keys j

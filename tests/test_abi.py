@@ -1,0 +1,155 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function include/focus.h
+declares, and rejects invalid arguments on the host (nothing is launched, no device touched)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "focus.h")
+
+F = pytest.importorskip("decodability_aware_token_amd.binding")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(focus_[a-z0-9_]+)\s*\(", src,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("focus_score_l01", "focus_select_budget", "focus_compact",
+              "focus_ragged_paged_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = F.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in F.SIGNATURES, name
+
+
+def test_status_strings_and_version():
+    assert F.status_string(0) == "ok"
+    assert "workspace" in F.status_string(-3)
+    assert F.lib().focus_version() >= 100
+
+
+P = 0x10000  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def _score(**kw):
+    a = dict(q0=P, k0=P, q1=P, k1=P, dt=1, B=4, blk=32, Hq=32, Hkv=8, d=128, sc=0.1, delta=P,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    return F.lib().focus_score_l01(a["q0"], a["k0"], a["q1"], a["k1"], a["dt"], a["B"], a["blk"],
+                                   a["Hq"], a["Hkv"], a["d"], a["sc"], a["delta"], a["ws"],
+                                   a["wsb"], None)
+
+
+def test_score_errors():
+    assert _score(q0=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _score(delta=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _score(B=0) == F.FOCUS_ERR_INVALID_ARG
+    assert _score(sc=0.0) == F.FOCUS_ERR_INVALID_ARG
+    assert _score(sc=float("nan")) == F.FOCUS_ERR_INVALID_ARG
+    assert _score(Hq=30) == F.FOCUS_ERR_INVALID_ARG          # Hq % Hkv != 0
+    assert _score(Hq=128, Hkv=8) == F.FOCUS_ERR_UNSUPPORTED  # G = 16
+    assert _score(blk=24) == F.FOCUS_ERR_UNSUPPORTED
+    assert _score(blk=128) == F.FOCUS_ERR_UNSUPPORTED
+    assert _score(d=96) == F.FOCUS_ERR_UNSUPPORTED
+    assert _score(dt=7) == F.FOCUS_ERR_UNSUPPORTED
+    assert _score(B=5000) == F.FOCUS_ERR_UNSUPPORTED
+    assert _score(q1=P + 8) == F.FOCUS_ERR_INVALID_ARG       # misaligned
+    assert _score(ws=None) == F.FOCUS_ERR_WORKSPACE
+    need = F.lib().focus_score_l01_workspace_size(4, 32, 32, 8, 128)
+    assert need == 4 * 8 * 32 * 4
+    assert _score(wsb=need - 1) == F.FOCUS_ERR_WORKSPACE
+
+
+def _select(**kw):
+    a = dict(delta=P, masked=P, budget=P, ad=0, beta=0.5, lo=2, hi=16, B=4, blk=32, keep=P,
+             kept=P)
+    a.update(kw)
+    return F.lib().focus_select_budget(a["delta"], a["masked"], a["budget"], a["ad"], a["beta"],
+                                       a["lo"], a["hi"], a["B"], a["blk"], a["keep"], a["kept"],
+                                       None)
+
+
+def test_select_errors():
+    assert _select(delta=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _select(budget=None) == F.FOCUS_ERR_INVALID_ARG     # fixed rule needs budgets
+    assert _select(kept=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _select(ad=1, lo=5, hi=2) == F.FOCUS_ERR_INVALID_ARG
+    assert _select(ad=1, beta=float("inf")) == F.FOCUS_ERR_INVALID_ARG
+    assert _select(B=-1) == F.FOCUS_ERR_INVALID_ARG
+    assert _select(blk=48) == F.FOCUS_ERR_UNSUPPORTED
+    assert _select(blk=8) == F.FOCUS_ERR_UNSUPPORTED
+
+
+def _compact(**kw):
+    a = dict(keep=P, B=4, blk=32, rows=P, rb=8192, cap=128, off=P, pos=P, gat=P)
+    a.update(kw)
+    return F.lib().focus_compact(a["keep"], a["B"], a["blk"], a["rows"], a["rb"], a["cap"],
+                                 a["off"], a["pos"], a["gat"], None)
+
+
+def test_compact_errors():
+    assert _compact(keep=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _compact(off=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _compact(gat=None) == F.FOCUS_ERR_INVALID_ARG      # rows without a destination
+    assert _compact(rows=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _compact(cap=-1) == F.FOCUS_ERR_INVALID_ARG
+    assert _compact(rb=0) == F.FOCUS_ERR_INVALID_ARG
+    assert _compact(rb=8200) == F.FOCUS_ERR_UNSUPPORTED       # not a multiple of 16
+    assert _compact(keep=P + 2) == F.FOCUS_ERR_INVALID_ARG    # keep must be 4-byte aligned
+    assert _compact(blk=20) == F.FOCUS_ERR_UNSUPPORTED
+    assert _compact(B=4097) == F.FOCUS_ERR_UNSUPPORTED
+
+
+def _attn(**kw):
+    a = dict(q=P, off=P, cap=64, kc=P, vc=P, npages=100, pt=P, maxp=16, pl=P, kb=P, vb=P, B=4,
+             blk=32, Hq=32, Hkv=8, d=128, S=64, mk=4, sc=0.088, out=P, lse=P, ws=P,
+             wsb=1 << 40)
+    a.update(kw)
+    return F.lib().focus_ragged_paged_attn(a["q"], a["off"], a["cap"], a["kc"], a["vc"],
+                                           a["npages"], a["pt"], a["maxp"], a["pl"], a["kb"],
+                                           a["vb"], a["B"], a["blk"], a["Hq"], a["Hkv"], a["d"],
+                                           a["S"], a["mk"], a["sc"], a["out"], a["lse"], a["ws"],
+                                           a["wsb"], None)
+
+
+def test_attn_errors():
+    assert _attn(q=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(out=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(kc=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(pt=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(npages=0) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(mk=0) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(mk=33) == F.FOCUS_ERR_INVALID_ARG            # max_kept > blk
+    assert _attn(sc=-1.0) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(Hq=12) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(S=8) == F.FOCUS_ERR_UNSUPPORTED
+    assert _attn(S=48) == F.FOCUS_ERR_UNSUPPORTED
+    assert _attn(d=256) == F.FOCUS_ERR_UNSUPPORTED
+    assert _attn(Hq=64, Hkv=4) == F.FOCUS_ERR_UNSUPPORTED     # G = 16
+    assert _attn(out=P + 4) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(maxp=1 << 20) == F.FOCUS_ERR_UNSUPPORTED
+    # long prefixes need a split workspace
+    need = F.attn_workspace_bytes(4, 32, 32, 8, 128, 64, 128, 4)
+    assert need > 0
+    assert _attn(maxp=128, ws=None) == F.FOCUS_ERR_WORKSPACE
+    assert _attn(maxp=128, wsb=need - 1) == F.FOCUS_ERR_WORKSPACE
+
+
+def test_attn_plan_is_bounded():
+    # the workspace grows with batch, heads and maximal prefix, never with the data
+    small = F.attn_workspace_bytes(64, 32, 16, 4, 128, 16, 512, 4)
+    big = F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 64, 4)
+    assert 0 < small < (256 << 20) and 0 < big < (256 << 20)
+    # short prefixes need no split, hence no workspace
+    assert F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 8, 4) == 0

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on seeded inputs.
+
+Every recipe runs end to end at a reduced batch (every element compared) and at its full size
+(scores, selections, offsets and gathers compared everywhere; attention on sampled requests,
+whose rows the oracle computes one by one).  Isolated tests cover each call's edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decodability_aware_token_amd import binding as F
+from parity_helpers import (DELTA_TOL, LSE_TOL, OUT_TOL, attn_case_inputs, bf16_to_np,
+                            check_keep, compare_attention, oracle_attention, run_gpu_step,
+                            step_inputs)
+from workloads import BY_NAME, make_step
+from workloads.torch_io import bf16_tensor
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# reduced batches of every recipe: oracle runs in seconds, still several tiles and ragged tails
+SMALL = {
+    "tiny_b2_blk16": {},
+    "sdar_b32_blk32": {"B": 12},
+    "sdar_b256_blk32": {"B": 24},
+    "sweep_b128_blk64": {"B": 10},
+    "sweep_b128_blk16": {"B": 12},
+    "longctx_b64_blk32": {"B": 4},
+}
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _end_to_end(st, cap=None):
+    ref = O.step(st)
+    fs, gpu = run_gpu_step(st, cap=cap)
+    derr = np.abs(gpu["delta"] - ref["delta"]).max()
+    assert derr <= DELTA_TOL, f"delta error {derr}"
+    excused = check_keep(gpu["keep"], ref["keep"], ref["delta"], st.masked, st.rule,
+                         gpu["kept_count"])
+    if st.rule[0] == "fixed" and not excused:
+        assert np.array_equal(gpu["offsets"], ref["offsets"])
+        assert np.array_equal(gpu["kept_pos"], ref["kept_pos"][: len(gpu["kept_pos"])])
+    if st.rule[0] == "fixed":
+        assert np.array_equal(gpu["offsets"], ref["offsets"])  # counts never depend on delta
+    oerr, lerr = compare_attention(gpu, ref, st.B, excused)
+    if "hidden_rows" in gpu and not excused:
+        T = len(gpu["kept_pos"])
+        assert np.array_equal(gpu["hidden_rows"], ref["gathered_hidden"][:T])
+    return derr, oerr, lerr, len(excused)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step_reduced_batch(name):
+    st = make_step(BY_NAME[name].scaled(**SMALL[name]))
+    _announce(f"step {name} reduced {SMALL[name]}")
+    derr, oerr, lerr, nex = _end_to_end(st)
+    print(f"delta err {derr:.2e} out err {oerr:.2e} lse err {lerr:.2e} excused {nex}")
+
+
+@pytest.mark.parametrize("name", ["sdar_b32_blk32", "sdar_b256_blk32", "sweep_b128_blk64",
+                                  "sweep_b128_blk16", "longctx_b64_blk32"])
+def test_step_full_size(name):
+    st = make_step(BY_NAME[name])
+    _announce(f"step {name} full size B={st.B}")
+    delta = O.score_l01(st.q0, st.k0, st.q1, st.k1, st.sm_scale, st.score_dtype)
+    keep, kept = O.select_budget(delta, st.masked, st.budget, st.rule)
+    offsets, kept_pos, _ = O.compact(keep)
+    fs, gpu = run_gpu_step(st)
+    derr = np.abs(gpu["delta"] - delta).max()
+    assert derr <= DELTA_TOL, f"delta error {derr}"
+    excused = check_keep(gpu["keep"], keep, delta, st.masked, st.rule, gpu["kept_count"])
+    if st.rule[0] == "fixed":
+        assert np.array_equal(gpu["offsets"], offsets)
+    if not excused:
+        assert np.array_equal(gpu["kept_pos"], kept_pos)
+    if "hidden_rows" in gpu:
+        # gathered rows are the kept rows of the GPU's own kept list, byte for byte
+        owner = np.repeat(np.arange(st.B), np.diff(gpu["offsets"]))
+        assert np.array_equal(gpu["hidden_rows"], st.hidden[owner, gpu["kept_pos"]])
+    # attention on sampled requests: the oracle computes those rows one request at a time,
+    # from the GPU-independent oracle-selected queries compared against the same GPU rows
+    rng = np.random.default_rng(7)
+    sample = rng.choice(st.B, size=min(st.B, 24), replace=False)
+    sample = [r for r in sample if r not in excused]
+    sample.append(int(np.argmax(st.prefix_len)))           # the longest prefix
+    sample = sorted(set(sample))
+    q64 = O.bf16_to_f64(st.q_att)
+    owner = np.repeat(np.arange(st.B), np.diff(offsets))
+    _, out, lse = oracle_attention(st, q64[owner, kept_pos], offsets, requests=sample)
+    goff = gpu["offsets"]
+    grows = np.concatenate([np.arange(goff[r], goff[r + 1]) for r in sample]).astype(np.int64)
+    gidx = torch.as_tensor(grows, device=DEV)
+    gout = fs.out[gidx].float().cpu().numpy()
+    glse = fs.lse[gidx].cpu().numpy()
+    oerr = np.abs(gout - out).max()
+    lerr = np.abs(glse - lse).max()
+    assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
+    print(f"delta err {derr:.2e} out err {oerr:.2e} lse err {lerr:.2e} excused {len(excused)}")
+
+
+# ------------------------------------------------------------------------------- selection
+@pytest.mark.parametrize("blk", [16, 32, 64])
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_select_isolated(blk, adaptive):
+    _announce(f"select blk={blk} adaptive={adaptive}")
+    rng = np.random.default_rng(100 + blk)
+    B = 300
+    delta = np.round(rng.standard_normal((B, blk)) * 4) / 8  # many exact ties
+    delta = delta.astype(np.float32)
+    masked = (rng.random((B, blk)) < 0.6).astype(np.uint8)
+    masked[0] = 0                                            # a request with nothing masked
+    masked[1] = 1
+    budget = rng.integers(-2, blk + 3, size=B).astype(np.int32)
+    rule = ("adaptive", 0.5, 2, 16) if adaptive else ("fixed",)
+    keep, kept = O.select_budget(delta.astype(np.float64), masked,
+                                 None if adaptive else budget, rule)
+    gk, gc = F.select_budget(torch.from_numpy(delta).to(DEV), torch.from_numpy(masked).to(DEV),
+                             None if adaptive else torch.from_numpy(budget).to(DEV),
+                             adaptive=rule[1:] if adaptive else None)
+    gk, gc = gk.cpu().numpy(), gc.cpu().numpy()
+    if adaptive:
+        check_keep(gk, keep, delta.astype(np.float64), masked, rule, gc)
+    else:
+        assert np.array_equal(gk, keep) and np.array_equal(gc, kept)
+
+
+# ------------------------------------------------------------------------------- compaction
+@pytest.mark.parametrize("blk,B,row_bytes,capfrac", [(16, 7, 16, 1.0), (32, 256, 8192, 1.0),
+                                                     (64, 33, 96, 0.3), (32, 1, 256, 0.0),
+                                                     (64, 1500, 32, 1.0)])
+def test_compact_isolated(blk, B, row_bytes, capfrac):
+    _announce(f"compact blk={blk} B={B} row_bytes={row_bytes} cap={capfrac}")
+    rng = np.random.default_rng(blk * 1000 + B)
+    keep = (rng.random((B, blk)) < 0.15).astype(np.uint8)
+    keep[rng.random(B) < 0.2] = 0                            # requests keeping nothing
+    rows = rng.integers(0, 256, size=(B, blk, row_bytes), dtype=np.uint8)
+    T = int(keep.sum())
+    cap = int(T * capfrac)
+    offsets, kept_pos, gathered = O.compact(keep, rows, cap=cap)
+    go, gp, gg = F.compact(torch.from_numpy(keep).to(DEV), torch.from_numpy(rows).to(DEV), cap=cap)
+    assert np.array_equal(go.cpu().numpy(), offsets)
+    assert np.array_equal(gp[:cap].cpu().numpy(), kept_pos)
+    assert np.array_equal(gg[:cap].cpu().numpy(), gathered)
+    # offsets only
+    go2, _, _ = F.compact(torch.from_numpy(keep).to(DEV), None, cap=cap, with_pos=False)
+    assert np.array_equal(go2.cpu().numpy(), offsets)
+
+
+# ------------------------------------------------------------------------------- attention
+def _random_keep(rng, B, blk, max_kept, empty_frac=0.1):
+    keep = np.zeros((B, blk), dtype=np.uint8)
+    for r in range(B):
+        if rng.random() < empty_frac:
+            continue
+        k = int(rng.integers(1, max_kept + 1))
+        keep[r, rng.choice(blk, size=k, replace=False)] = 1
+    return keep
+
+
+ATTN_CASES = {
+    # name: (recipe, overrides, max_kept)
+    "g4_d128_s64": ("sdar_b32_blk32", {"B": 9}, 4),
+    "g4_q32rows": ("sdar_b32_blk32", {"B": 6}, 8),
+    "g4_q64rows_blk64": ("sweep_b128_blk64", {"B": 5}, 16),
+    "blk16_s64": ("sweep_b128_blk16", {"B": 7}, 4),
+    "g1_d64_s16": ("tiny_b2_blk16", {"B": 5, "prefix": ("uniform", 0, 64)}, 4),
+    "g2_d64_s32": ("tiny_b2_blk16", {"B": 6, "Hq": 8, "Hkv": 4, "S": 32,
+                                     "prefix": ("uniform", 1, 300), "max_prefix": 320}, 8),
+    "g8_d128_s16_split": ("longctx_b64_blk32", {"B": 3, "Hq": 16, "Hkv": 2,
+                                                "prefix": ("uniform", 3000, 5000),
+                                                "max_prefix": 5000}, 2),
+    "g4_long_split": ("longctx_b64_blk32", {"B": 4}, 4),
+}
+
+
+@pytest.mark.parametrize("case", list(ATTN_CASES))
+def test_attn_isolated(case):
+    name, over, max_kept = ATTN_CASES[case]
+    over = dict(over)
+    over.setdefault("budget", ("fixed", max_kept))
+    over["score_dtype"] = "bf16"
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"attn {case} B={st.B} G={st.Hq // st.Hkv} d={st.d} S={st.S} blk={st.blk} "
+              f"max_kept={max_kept} prefix_max={int(st.prefix_len.max())}")
+    rng = np.random.default_rng(hash(case) % 1000)
+    keep = _random_keep(rng, st.B, st.blk, max_kept)
+    c = attn_case_inputs(st, keep)
+    ref_out, ref_lse = oracle_attention(st, c["q_rows64"], c["offsets"])
+    t = step_inputs(st)
+    out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache, t.page_table,
+                                   t.prefix_len, t.k_blk, t.v_blk, max_kept, st.sm_scale)
+    torch.cuda.synchronize()
+    T = int(c["offsets"][-1])
+    go = out[:T].float().cpu().numpy()
+    gl = lse[:T].cpu().numpy()
+    oerr = np.abs(go - ref_out).max() if T else 0.0
+    lerr = np.abs(gl - ref_lse).max() if T else 0.0
+    assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
+    print(f"T={T} out err {oerr:.2e} lse err {lerr:.2e}")
+
+
+def test_attn_peaky_inputs_and_cap():
+    # unscaled N(0,1) queries make the softmax peaky (rescaling of the running max matters);
+    # cap below T leaves the rows past cap untouched
+    st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=8))
+    _announce("attn peaky + cap")
+    rng = np.random.default_rng(3)
+    keep = _random_keep(rng, st.B, st.blk, 4, empty_frac=0.0)
+    c = attn_case_inputs(st, keep)
+    from workloads import f32_to_bf16_bits
+    qbits = f32_to_bf16_bits(rng.standard_normal(c["q_bits"].shape).astype(np.float32) * 3.0)
+    q64 = O.bf16_to_f64(qbits)
+    T = int(c["offsets"][-1])
+    cap = T - 5
+    ref_out, ref_lse = oracle_attention(st, q64, c["offsets"], cap=cap)
+    t = step_inputs(st)
+    sentinel = torch.full((T, st.Hq, st.d), 7.0, dtype=torch.bfloat16, device=DEV)
+    dq = bf16_tensor(qbits[:cap], DEV)
+    out, lse = F.ragged_paged_attn(dq, c["d_offsets"], t.k_cache, t.v_cache, t.page_table,
+                                   t.prefix_len, t.k_blk, t.v_blk, 4, st.sm_scale,
+                                   out=sentinel[:cap])
+    torch.cuda.synchronize()
+    oerr = np.abs(out.float().cpu().numpy() - ref_out).max()
+    lerr = np.abs(lse.cpu().numpy() - ref_lse).max()
+    assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
+    assert torch.all(sentinel[cap:] == 7.0)
+
+
+def test_attn_poisoned_unused_memory_is_never_read():
+    # NaN in every cache slot past a prefix and in spare pages, out-of-range ids past each
+    # request's last page: the result must equal the clean run bit for bit
+    _announce("attn poison")
+    rec = BY_NAME["longctx_b64_blk32"].scaled(B=4)
+    clean = make_step(rec)
+    pois = make_step(rec, poison=True)
+    keep = _random_keep(np.random.default_rng(5), rec.B, rec.blk, 4, empty_frac=0.0)
+    outs = []
+    for st in (clean, pois):
+        c = attn_case_inputs(st, keep)
+        t = step_inputs(st)
+        out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache,
+                                       t.page_table, t.prefix_len, t.k_blk, t.v_blk, 4,
+                                       st.sm_scale)
+        torch.cuda.synchronize()
+        outs.append((bf16_to_np(out), lse.cpu().numpy()))
+    assert np.isfinite(outs[1][1][: int(keep.sum())]).all()
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_attn_invalid_device_data_gives_nan_rows():
+    _announce("attn invalid page id / prefix length")
+    st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=6))
+    keep = _random_keep(np.random.default_rng(9), st.B, st.blk, 4, empty_frac=0.0)
+    c = attn_case_inputs(st, keep)
+    t = step_inputs(st)
+    ref, ref_lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache,
+                                       t.page_table, t.prefix_len, t.k_blk, t.v_blk, 4,
+                                       st.sm_scale)
+    pt = t.page_table.clone()
+    pt[1, 0] = st.num_pages + 5          # request 1: a used page id out of range
+    pl = t.prefix_len.clone()
+    pl[3] = -4                           # request 3: negative prefix length
+    out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache, pt, pl,
+                                   t.k_blk, t.v_blk, 4, st.sm_scale)
+    torch.cuda.synchronize()
+    off = c["offsets"]
+    for r in range(st.B):
+        rows = slice(int(off[r]), int(off[r + 1]))
+        if r in (1, 3):
+            assert torch.isnan(out[rows].float()).all() and torch.isnan(lse[rows]).all()
+        else:
+            assert torch.equal(out[rows], ref[rows]) and torch.equal(lse[rows], ref_lse[rows])
+
+
+def test_step_edge_cases_empty_prefix_and_nothing_masked():
+    _announce("step edge cases")
+    rec = BY_NAME["sdar_b32_blk32"].scaled(B=6, prefix=("uniform", 0, 200), budget=("fixed", 3))
+    plen = np.array([0, 1, 31, 32, 33, 200])
+    mcount = np.array([20, 0, 32, 25, 1, 20])    # request 1 has nothing masked: keeps nothing
+    st = make_step(rec, prefix_override=plen, masked_override=mcount)
+    derr, oerr, lerr, nex = _end_to_end(st)
+    print(f"delta err {derr:.2e} out err {oerr:.2e} lse err {lerr:.2e}")
+
+
+def test_deterministic_bitwise():
+    _announce("determinism")
+    st = make_step(BY_NAME["longctx_b64_blk32"].scaled(B=8))
+    fs, a = run_gpu_step(st)
+    fs.run()
+    torch.cuda.synchronize()
+    from parity_helpers import fetch
+    b = fetch(fs)
+    assert np.array_equal(a["delta"], b["delta"])
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.array_equal(a["lse"], b["lse"])
