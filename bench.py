@@ -1,0 +1,216 @@
+"""Throughput of the focused block-diffusion step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: importance scoring (layer 1 minus
+layer 0), budgeted top-k selection, compaction + gather of the hidden states and of the
+attention queries, and ragged paged attention over each request's paged prefix plus block KV.
+Inputs are seeded synthetic tensors already resident in HBM.  One JSON line is printed.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_algorithmic(st, kept):
+    """Bytes and flops the attention must move/do: per request with k_r > 0, its whole prefix
+    plus block K and V once, its queries, outputs, LSE, page-table entries and two ints."""
+    P = st.prefix_len.astype(np.int64)
+    k = kept.astype(np.int64)
+    act = k > 0
+    kv = ((P + st.blk) * st.Hkv * st.d * 2 * 2)[act].sum()
+    qo = (k * st.Hq * st.d * 2 * 2).sum()
+    ls = (k * st.Hq * 4).sum()
+    tab = (4 * ((P + st.S - 1) // st.S))[act].sum() + 8 * act.sum()
+    flops = (4 * k * st.Hq * (P + st.blk) * st.d).sum()
+    return int(kv + qo + ls + tab), int(flops)
+
+
+def score_algorithmic(st):
+    es = 4 if st.score_dtype == "f32" else 2
+    by = 2 * st.B * st.blk * (st.Hq + st.Hkv) * st.d * es + 4 * st.B * st.blk
+    fl = 2 * 2 * st.B * st.blk * st.blk * st.Hq * st.d
+    return by, fl
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attn.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "decodability_aware_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attn_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(recipe, budget_s):
+    """The fp64 oracle timed on a bounded sample of the same workload (fewer requests drawn from
+    the same distributions), scaled to focused tokens per second."""
+    import oracle
+    from workloads import make_step
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    Bs = 16
+    total_t, total_tok, reqs = 0.0, 0, 0
+    seed = recipe.seed
+    while total_t < budget_s and reqs < recipe.B:
+        st = make_step(recipe.scaled(B=Bs), seed=seed)
+        t0 = time.perf_counter()
+        res = oracle.step(st)
+        total_t += time.perf_counter() - t0
+        total_tok += int(res["offsets"][-1])
+        reqs += Bs
+        seed += 1
+    return {"value": total_tok / total_t, "unit": "focused tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reqs} requests of {recipe.name} in batches of {Bs} (seeds from "
+                      f"{recipe.seed}), full step score+select+compact+attend in fp64, "
+                      f"{total_t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sdar_b256_blk32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md "
+              "for how the step would shard by request).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decodability_aware_token_amd import FocusStep, StepInputs
+    from workloads import BY_NAME, make_step
+    from workloads.torch_io import upload
+
+    recipe = BY_NAME[args.workload]
+    log(f"[bench] generating {recipe.name}")
+    st = make_step(recipe)
+    dev = torch.device("cuda:0")
+    t = upload(st, dev)
+    inp = StepInputs(**{k: t[k] for k in ("q0", "k0", "q1", "k1", "masked", "budget", "adaptive",
+                                           "max_kept", "q_att", "k_cache", "v_cache",
+                                           "page_table", "prefix_len", "k_blk", "v_blk",
+                                           "sm_scale", "hidden")})
+    fs = FocusStep(inp)
+    stream = torch.cuda.current_stream(dev)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        fs.run()
+    torch.cuda.synchronize()
+
+    stages = ("score", "select", "compact_hidden", "compact_q", "attend")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, name in enumerate(stages):
+            getattr(fs, name)()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = np.zeros(len(stages))
+    step_ms = np.zeros(args.steps)
+    for i in range(args.steps):
+        for j in range(len(stages)):
+            per_stage[j] += ev[i][j].elapsed_time(ev[i][j + 1])
+        step_ms[i] = ev[i][0].elapsed_time(ev[i][-1])
+    per_stage /= args.steps
+    ms_per_step = wall * 1000.0 / args.steps
+
+    offsets = fs.offsets.cpu().numpy()
+    kept = np.diff(offsets)
+    T = int(offsets[-1])
+    attn_bytes, attn_flops = attn_algorithmic(st, kept)
+    attn_ms = per_stage[stages.index("attend")]
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    sb, sf = score_algorithmic(st)
+    for j, name in enumerate(stages):
+        log(f"[bench] {name:15s} {per_stage[j] * 1000:9.1f} us")
+    log(f"[bench] step (events) {step_ms.mean() * 1000:.1f} us median {np.median(step_ms) * 1000:.1f}"
+        f" us; wall {ms_per_step * 1000:.1f} us; T={T}")
+    log(f"[bench] attention {attn_bytes / 1e6:.1f} MB algorithmic -> {achieved:.0f} GB/s "
+        f"({achieved / PEAK_HBM_GBS * 100:.1f}% of HBM), "
+        f"{attn_flops / (attn_ms * 1e-3) / 1e12:.2f} TFLOP/s")
+    sc_ms = per_stage[0]
+    log(f"[bench] score {sb / 1e6:.1f} MB -> {sb / (sc_ms * 1e-3) / 1e9:.0f} GB/s, "
+        f"{sf / (sc_ms * 1e-3) / 1e12:.2f} TFLOP/s")
+
+    res = {
+        "metric": "focused block-tokens/s per diffusion step",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "focused tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no weights or datasets)",
+        "config": {
+            "workload": recipe.name, "global_batch": st.B, "block": st.blk, "Hq": st.Hq,
+            "Hkv": st.Hkv, "head_dim": st.d, "page": st.S,
+            "prefix": f"{recipe.prefix}", "budget": f"{recipe.budget}",
+            "hidden": recipe.hidden, "kept_tokens": T, "block_tokens": st.B * st.blk,
+            "block_tokens_per_s": st.B * st.blk / (ms_per_step * 1e-3),
+            "stage_us": {n: round(per_stage[j] * 1000, 2) for j, n in enumerate(stages)},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "ragged paged attention (focus_ragged_paged_attn)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": counter_traffic(recipe.name),
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "avg_launch_us": round(attn_ms * 1000, 2),
+            "mfma_util": round(attn_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
+        res["cpu_baseline"] = cpu_baseline(recipe, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,8 +26,11 @@
 namespace focus {
 namespace {
 
+#ifndef FOCUS_ATTN_MAX_TILES_PER_SPLIT
+#define FOCUS_ATTN_MAX_TILES_PER_SPLIT 32
+#endif
 constexpr int kWaves = 4;
-constexpr int kMaxTilesPerSplit = 32;
+constexpr int kMaxTilesPerSplit = FOCUS_ATTN_MAX_TILES_PER_SPLIT;  // 32-key tiles per work item
 
 struct Params {
   const uint16_t* q;
@@ -54,101 +57,70 @@ struct Tile {
 };
 
 // Loads tile `it` of the item's key sequence (prefix tiles first, then block tiles) into T.
-// Keys at or past the segment's valid length are not loaded (K garbage is masked later; a V
-// chunk straddling the end has its invalid keys zeroed so 0 * garbage cannot appear).
+// Branch-free, so the compiler can keep the next tile's loads in flight (it counts them): each
+// lane's 8-key group is clamped to the group holding the segment's last valid key, which always
+// lies in an allocated page, and the keys past the valid length are masked in compute_tile.  An
+// out-of-range page id is replaced by page 0 and reported through `bad`.
 template <int D>
 __device__ __forceinline__ void load_tile(Tile<D>& T, const Params& p, int it, int ntp, int P,
                                           int r, int g, const int* s_pages, int pg0, int lane,
                                           bool& bad) {
   constexpr int NK = D / 32, ND = D / 16;
   const int m16 = lane & 15, j4 = lane >> 4;
-  int key0, nvalid, log2S;
-  bool paged = it < ntp;
-  if (paged) {
-    key0 = it * 32;
-    nvalid = P;
-    log2S = p.log2S;
-  } else {
-    key0 = (it - ntp) * 32;
-    nvalid = p.blk;
-    log2S = p.log2blk;
-  }
+  const bool paged = it < ntp;  // wave-uniform
+  const int key0 = paged ? it * 32 : (it - ntp) * 32;
+  const int nvalid = paged ? P : p.blk;
+  const int log2S = paged ? p.log2S : p.log2blk;
   const int S = 1 << log2S;
   const size_t page_elems = (size_t)D << log2S;  // one (page, kv head) block
+  const int last_group = (nvalid - 1) & ~7;
 
-  // K: two keys per lane (subtiles s = 0, 1), always in the same 8-key group -> same page.
-  const int kkey = key0 + 8 * (m16 >> 2) + (m16 & 3);
-  {
-    const bool valid = kkey < nvalid;
-    const uint16_t* base = nullptr;
-    if (valid) {
-      if (paged) {
-        const int pid = s_pages[(kkey >> log2S) - pg0];
-        if (pid < 0 || pid >= p.num_pages) {
-          bad = true;
-        } else {
-          base = p.k_cache + ((size_t)pid * p.Hkv + g) * page_elems;
-        }
-      } else {
-        base = p.k_blk + ((size_t)r * p.Hkv + g) * page_elems;
-      }
-    }
-    const int slot = kkey & (S - 1);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        if (base != nullptr && kkey + 4 * s < nvalid)
-          T.k[s][kk] = load16v(base + ((((4 * kk + j4) << log2S) + slot + 4 * s) << 3));
-        else
-          T.k[s][kk] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+  // K: keys kg + (m16 & 3) + 4*s of the lane's 8-key group kg (s = 0, 1: the two subtiles)
+  const int kg = min(key0 + 8 * (m16 >> 2), last_group);
+  // V: the 8 keys vg .. vg+7 of lane group j4
+  const int vg = min(key0 + 8 * j4, last_group);
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  if (paged) {
+    int pk = s_pages[(kg >> log2S) - pg0];
+    int pv = s_pages[(vg >> log2S) - pg0];
+    const bool okk = pk >= 0 && pk < p.num_pages, okv = pv >= 0 && pv < p.num_pages;
+    bad = bad || !okk || !okv;
+    pk = okk ? pk : 0;
+    pv = okv ? pv : 0;
+    kbase = p.k_cache + ((size_t)pk * p.Hkv + g) * page_elems;
+    vbase = p.v_cache + ((size_t)pv * p.Hkv + g) * page_elems;
+  } else {
+    kbase = p.k_blk + ((size_t)r * p.Hkv + g) * page_elems;
+    vbase = p.v_blk + ((size_t)r * p.Hkv + g) * page_elems;
   }
-  // V: 8 keys (one 16-byte chunk per dim) per lane group.
-  {
-    const int vkey = key0 + 8 * j4;
-    const bool valid = vkey < nvalid;
-    const uint16_t* base = nullptr;
-    if (valid) {
-      if (paged) {
-        const int pid = s_pages[(vkey >> log2S) - pg0];
-        if (pid < 0 || pid >= p.num_pages) {
-          bad = true;
-        } else {
-          base = p.v_cache + ((size_t)pid * p.Hkv + g) * page_elems;
-        }
-      } else {
-        base = p.v_blk + ((size_t)r * p.Hkv + g) * page_elems;
-      }
-    }
-    const int slot = vkey & (S - 1);
-    const int nv = nvalid - vkey;  // valid keys in this chunk (if < 8)
+  const int kslot = (kg & (S - 1)) + (m16 & 3);
+  const uint16_t* kp = kbase + ((size_t)((j4 << log2S) + kslot) << 3);
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      u32x4_t x = u32x4_t{0u, 0u, 0u, 0u};
-      if (base != nullptr) x = load16v(base + (((slot >> 3) * D + 16 * dt + m16) << 3));
-      if (nv < 8) {
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if (2 * w >= nv)
-            x[w] = 0u;
-          else if (2 * w + 1 >= nv)
-            x[w] &= 0xffffu;
-        }
-      }
-      T.v[dt] = x;
-    }
-  }
+    for (int kk = 0; kk < NK; ++kk)
+      T.k[s][kk] = load16v(kp + ((size_t)(((4 * kk) << log2S) + 4 * s) << 3));
+  const uint16_t* vp = vbase + ((size_t)((vg & (S - 1)) >> 3) * D + m16) * 8;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) T.v[dt] = load16v(vp + 16 * dt * 8);
 }
 
 template <int D, int QT>
-__device__ __forceinline__ void compute_tile(const Tile<D>& T, int key0, int nvalid,
+__device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
                                              const u32x4_t (&qf)[QT][D / 32],
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
                                              float (&lrun)[QT], float scale_log2, int lane) {
   constexpr int NK = D / 32, ND = D / 16;
   const int j4 = lane >> 4;
   const int kbase = key0 + 8 * j4;  // this lane group's 8 keys: kbase + 0..7
+  // Values of keys past the end are zeroed: their weights are zero, but the loaded values may
+  // be anything and 0 * NaN would not vanish.  Branch-free (all-ones masks on full tiles).
+  const int nv = nvalid - kbase;
+  u32x4_t vmask;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    vmask[w] = (2 * w + 1 < nv) ? 0xffffffffu : ((2 * w < nv) ? 0x0000ffffu : 0u);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -163,11 +135,8 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& T, int key0, int nva
       x[i] = s0[i] * scale_log2;
       x[4 + i] = s1[i] * scale_log2;
     }
-    if (kbase + 8 > nvalid) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (kbase + e >= nvalid) x[e] = -INFINITY;
-    }
+    for (int e = 0; e < 8; ++e) x[e] = (e < nv) ? x[e] : -INFINITY;
     float mx = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
@@ -196,7 +165,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& T, int key0, int nva
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
       o[qt][dt] *= alpha;
-      o[qt][dt] = mfma_bf16(T.v[dt], pf, o[qt][dt]);
+      o[qt][dt] = mfma_bf16(T.v[dt] & vmask, pf, o[qt][dt]);
     }
   }
 }
@@ -212,7 +181,8 @@ __global__ __launch_bounds__(256, (QT >= 4 ? 1 : 2)) void attn_kernel(Params p) 
   __shared__ int s_pages[MAXPG];
   __shared__ int s_bad;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m16 = lane & 15, j4 = lane >> 4;
   const int BH = p.B * p.Hkv;
   const int rg = blockIdx.x % BH, split = blockIdx.x / BH;
@@ -270,27 +240,33 @@ __global__ __launch_bounds__(256, (QT >= 4 ? 1 : 2)) void attn_kernel(Params p) 
     for (int dt = 0; dt < ND; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Each wave streams tiles wave, wave+4, ... of [t0, t1), loading tile k+1 while it computes
+  // tile k.  The prefetch is unconditional (after the wave's last tile it re-reads that tile, a
+  // cache hit), so the wait before each compute only drains the older tile's loads.
   bool bad = false;
   Tile<D> ta, tb;
-  int it = t0 + wave;
-  if (it < t1) load_tile<D>(ta, p, it, ntp, P, r, g, s_pages, pg0, lane, bad);
-  while (it < t1) {
-    const int itb = it + kWaves;
-    if (itb < t1) load_tile<D>(tb, p, itb, ntp, P, r, g, s_pages, pg0, lane, bad);
-    {
-      const bool pg = it < ntp;
-      compute_tile<D, QT>(ta, pg ? it * 32 : (it - ntp) * 32, pg ? P : p.blk, qf, o, mrun, lrun,
-                          p.scale_log2, lane);
+  const int nk = t0 + wave < t1 ? (t1 - t0 - wave + kWaves - 1) / kWaves : 0;
+  auto tile_of = [&](int k) { return t0 + wave + kWaves * min(k, nk - 1); };
+  static_assert(kMaxTilesPerSplit % (2 * kWaves) == 0, "tile loop unrolls by two buffers");
+  auto seg_key0 = [&](int i) { return i < ntp ? i * 32 : (i - ntp) * 32; };
+  auto seg_len = [&](int i) { return i < ntp ? P : p.blk; };
+  if (nk > 0) {
+    // fully unrolled (a wave takes at most kMaxTilesPerSplit / kWaves tiles of a split), so the
+    // code is straight-line and the buffers alternate statically
+    load_tile<D>(ta, p, tile_of(0), ntp, P, r, g, s_pages, pg0, lane, bad);
+#pragma unroll
+    for (int k = 0; k < kMaxTilesPerSplit / kWaves; k += 2) {
+      load_tile<D>(tb, p, tile_of(k + 1), ntp, P, r, g, s_pages, pg0, lane, bad);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      int it = tile_of(k);
+      compute_tile<D, QT>(ta, seg_key0(it), seg_len(it), qf, o, mrun, lrun, p.scale_log2, lane);
+      if (k + 1 >= nk) break;
+      load_tile<D>(ta, p, tile_of(k + 2), ntp, P, r, g, s_pages, pg0, lane, bad);
+      __builtin_amdgcn_sched_barrier(0);
+      it = tile_of(k + 1);
+      compute_tile<D, QT>(tb, seg_key0(it), seg_len(it), qf, o, mrun, lrun, p.scale_log2, lane);
+      if (k + 2 >= nk) break;
     }
-    if (itb >= t1) break;
-    const int ita = itb + kWaves;
-    if (ita < t1) load_tile<D>(ta, p, ita, ntp, P, r, g, s_pages, pg0, lane, bad);
-    {
-      const bool pg = itb < ntp;
-      compute_tile<D, QT>(tb, pg ? itb * 32 : (itb - ntp) * 32, pg ? P : p.blk, qf, o, mrun,
-                          lrun, p.scale_log2, lane);
-    }
-    it = ita;
   }
 
   // Merge the 4 waves (fixed order), one 16-row query tile at a time, and write the result or

@@ -4,8 +4,8 @@
 // cards "Design" and "Decodability Signal"; the paper's abstract (attention-derived importance).
 //
 // Kernel 1 (score_partial): one workgroup per (request r, kv head g), 4 waves.  For each layer
-// the K tile of kv head g and the Q tiles of up to HS of its query heads are staged in LDS with
-// coalesced 16-byte loads.  A wave takes one (query head, 16-query tile) unit at a time and
+// the K tile of kv head g and the Q tiles of GS of its query heads are staged in LDS with
+// coalesced 16-byte loads, all issued before the LDS writes, with the next pass in flight.  A wave takes one (query head, 16-query tile) unit at a time and
 // computes S^T = K Q^T (keys x queries) on MFMA, so a lane holds one query's scores for 4 keys
 // of each 16-key tile: the row softmax over keys needs a local reduction plus two cross-lane
 // steps, and the column sums accumulate in registers across units and both layers (layer 0
@@ -17,28 +17,147 @@
 namespace focus {
 namespace {
 
-template <typename T, int BLK, int D>
+// One pass = one layer's K tile of kv head g plus the Q tiles of GS of its query heads.
+template <typename T, int BLK, int D, int GS>
+struct Pass {
+  static constexpr int VEC = 16 / sizeof(T);         // elements per 16-byte chunk
+  static constexpr int CH = D / VEC;                 // chunks per row
+  static constexpr int CHUNKS = BLK * CH * (1 + GS); // K rows, then Q rows of GS heads
+  static constexpr int PER_THREAD = (CHUNKS + 255) / 256;
+  uint4 v[PER_THREAD];
+};
+
+template <typename T, int BLK, int D, int GS>
+__device__ __forceinline__ void load_pass(Pass<T, BLK, D, GS>& ps, const T* Q, const T* K, int r,
+                                          int g, int Hq, int Hkv, int G, int h0, int tid) {
+  using PS = Pass<T, BLK, D, GS>;
+#pragma unroll
+  for (int u = 0; u < PS::PER_THREAD; ++u) {
+    const int c = tid + 256 * u;
+    if (PS::CHUNKS % 256 != 0 && c >= PS::CHUNKS) break;
+    const T* src;
+    if (c < BLK * PS::CH) {
+      const int row = c / PS::CH, cc = c % PS::CH;
+      src = K + ((size_t)(r * BLK + row) * Hkv + g) * D + cc * PS::VEC;
+    } else {
+      const int q = c - BLK * PS::CH;
+      const int row = q / (GS * PS::CH), rem = q % (GS * PS::CH);
+      const int hh = rem / PS::CH, cc = rem % PS::CH;
+      src = Q + ((size_t)(r * BLK + row) * Hq + g * G + h0 + hh) * D + cc * PS::VEC;
+    }
+    ps.v[u] = load16(src);
+  }
+}
+
+template <typename T, int BLK, int D, int GS>
+__device__ __forceinline__ void store_pass(const Pass<T, BLK, D, GS>& ps, T* Ks, T* Qs, int tid) {
+  using PS = Pass<T, BLK, D, GS>;
+  constexpr int ROW = D + PS::VEC;
+#pragma unroll
+  for (int u = 0; u < PS::PER_THREAD; ++u) {
+    const int c = tid + 256 * u;
+    if (PS::CHUNKS % 256 != 0 && c >= PS::CHUNKS) break;
+    T* dst;
+    if (c < BLK * PS::CH) {
+      const int row = c / PS::CH, cc = c % PS::CH;
+      dst = Ks + row * ROW + cc * PS::VEC;
+    } else {
+      const int q = c - BLK * PS::CH;
+      const int row = q / (GS * PS::CH), rem = q % (GS * PS::CH);
+      const int hh = rem / PS::CH, cc = rem % PS::CH;
+      dst = Qs + (row * GS + hh) * ROW + cc * PS::VEC;
+    }
+    *reinterpret_cast<uint4*>(dst) = ps.v[u];
+  }
+}
+
+// Column sums of the row softmax of S^T = K Q^T for one (query head, 16-query tile) unit,
+// accumulated into colacc with sign -1 (layer 0) or +1 (layer 1).
+template <typename T, int BLK, int D, int GS>
+__device__ __forceinline__ void score_unit(const T* Ks, const T* Qs, int hh, int nt, int n16,
+                                           int j4, float scale_log2, float sign,
+                                           float (&colacc)[BLK / 16][4]) {
+  constexpr int ES = sizeof(T);
+  constexpr int ROW = D + 16 / ES;
+  constexpr int NMT = BLK / 16;
+  f32x4_t acc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const T* qrow = Qs + ((16 * nt + n16) * GS + hh) * ROW;
+  if constexpr (ES == 2) {
+    constexpr int NK = D / 32;
+    u32x4_t qf[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      qf[kk] = *reinterpret_cast<const u32x4_t*>(qrow + (4 * kk + j4) * 8);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const T* krow = Ks + (16 * mt + n16) * ROW;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + (4 * kk + j4) * 8);
+        acc[mt] = mfma_bf16(a, qf[kk], acc[mt]);
+      }
+    }
+  } else {
+    constexpr int NK = D / 4;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const T* krow = Ks + (16 * mt + n16) * ROW;
+#pragma unroll 8
+      for (int kk = 0; kk < NK; ++kk)
+        acc[mt] = mfma_f32(krow[4 * kk + j4], qrow[4 * kk + j4], acc[mt]);
+    }
+  }
+  // acc[mt][i] = S[key 16mt + 4*j4 + i][query 16nt + n16]; softmax over all BLK keys.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[mt][i]);
+  mx = wave_max_xor(mx, 16);
+  mx = wave_max_xor(mx, 32);
+  float p[NMT][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[mt][i] = fast_exp2((acc[mt][i] - mx) * scale_log2);
+      sum += p[mt][i];
+    }
+  sum = wave_sum_xor(sum, 16);
+  sum = wave_sum_xor(sum, 32);
+  const float w = sign / sum;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) colacc[mt][i] += p[mt][i] * w;
+}
+
+// Passes run (layer, head group) in order; the next pass's global loads are in flight (in
+// registers) while the current one is computed from LDS.
+template <typename T, int BLK, int D, int GS>
 __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict__ q0,
                                                             const T* __restrict__ k0,
                                                             const T* __restrict__ q1,
                                                             const T* __restrict__ k1, int Hq,
-                                                            int Hkv, int HS, float scale_log2,
+                                                            int Hkv, float scale_log2,
                                                             float* __restrict__ part) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int ES = sizeof(T);
-  constexpr int VEC = 16 / ES;        // elements per 16-byte chunk
-  constexpr int ROW = D + VEC;        // padded LDS row (elements)
-  constexpr int CH = D / VEC;         // 16-byte chunks per row
-  constexpr int NMT = BLK / 16;       // 16-key (and 16-query) tiles
-  T* Ks = reinterpret_cast<T*>(smem);           // [BLK][ROW]
-  T* Qs = Ks + BLK * ROW;                       // [BLK][HS][ROW]
-  float* red = reinterpret_cast<float*>(Qs + BLK * HS * ROW);  // [4][BLK]
+  constexpr int ROW = D + 16 / sizeof(T);
+  constexpr int NMT = BLK / 16;
+  T* Ks = reinterpret_cast<T*>(smem);               // [BLK][ROW]
+  T* Qs = Ks + BLK * ROW;                            // [BLK][GS][ROW]
+  float* red = reinterpret_cast<float*>(Qs + BLK * GS * ROW);  // [4][BLK]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, j4 = lane >> 4;
   const int G = Hq / Hkv;
   const int r = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int groups = G / GS;        // head groups per layer
+  const int npass = 2 * groups;
 
   float colacc[NMT][4];
 #pragma unroll
@@ -46,83 +165,19 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i) colacc[mt][i] = 0.f;
 
-  for (int layer = 0; layer < 2; ++layer) {
-    const T* Q = layer ? q1 : q0;
-    const T* K = layer ? k1 : k0;
-    const float sign = layer ? 1.f : -1.f;
-    for (int h0 = 0; h0 < G; h0 += HS) {
-      const int hs = min(HS, G - h0);
-      __syncthreads();  // the previous stage's readers are done
-      for (int c = tid; c < BLK * CH; c += 256) {
-        const int row = c / CH, cc = c % CH;
-        const T* src = K + ((size_t)(r * BLK + row) * Hkv + g) * D + cc * VEC;
-        *reinterpret_cast<uint4*>(Ks + row * ROW + cc * VEC) = load16(src);
-      }
-      for (int c = tid; c < BLK * hs * CH; c += 256) {
-        const int row = c / (hs * CH), rem = c % (hs * CH);
-        const int hh = rem / CH, cc = rem % CH;
-        const T* src = Q + ((size_t)(r * BLK + row) * Hq + g * G + h0 + hh) * D + cc * VEC;
-        *reinterpret_cast<uint4*>(Qs + (row * HS + hh) * ROW + cc * VEC) = load16(src);
-      }
-      __syncthreads();
-
-      for (int u = wave; u < hs * NMT; u += 4) {
-        const int hh = u / NMT, nt = u % NMT;
-        f32x4_t acc[NMT];
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const T* qrow = Qs + ((16 * nt + n16) * HS + hh) * ROW;
-        if constexpr (ES == 2) {
-          constexpr int NK = D / 32;
-          u32x4_t qf[NK];
-#pragma unroll
-          for (int kk = 0; kk < NK; ++kk)
-            qf[kk] = *reinterpret_cast<const u32x4_t*>(qrow + (4 * kk + j4) * 8);
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            const T* krow = Ks + (16 * mt + n16) * ROW;
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-              const u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + (4 * kk + j4) * 8);
-              acc[mt] = mfma_bf16(a, qf[kk], acc[mt]);
-            }
-          }
-        } else {
-          constexpr int NK = D / 4;
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            const T* krow = Ks + (16 * mt + n16) * ROW;
-#pragma unroll 8
-            for (int kk = 0; kk < NK; ++kk)
-              acc[mt] = mfma_f32(krow[4 * kk + j4], qrow[4 * kk + j4], acc[mt]);
-          }
-        }
-        // acc[mt][i] = S[key 16mt + 4*j4 + i][query 16nt + n16]; softmax over all BLK keys.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[mt][i]);
-        mx = wave_max_xor(mx, 16);
-        mx = wave_max_xor(mx, 32);
-        float p[NMT][4];
-        float sum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[mt][i] = fast_exp2((acc[mt][i] - mx) * scale_log2);
-            sum += p[mt][i];
-          }
-        sum = wave_sum_xor(sum, 16);
-        sum = wave_sum_xor(sum, 32);
-        const float w = sign / sum;
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) colacc[mt][i] += p[mt][i] * w;
-      }
+  Pass<T, BLK, D, GS> ps;
+  load_pass<T, BLK, D, GS>(ps, q0, k0, r, g, Hq, Hkv, G, 0, tid);
+  for (int pi = 0; pi < npass; ++pi) {
+    if (pi > 0) __syncthreads();  // every wave is done with the previous pass's tiles
+    store_pass<T, BLK, D, GS>(ps, Ks, Qs, tid);
+    __syncthreads();
+    if (pi + 1 < npass) {
+      const int nl = (pi + 1) / groups, nh = ((pi + 1) % groups) * GS;
+      load_pass<T, BLK, D, GS>(ps, nl ? q1 : q0, nl ? k1 : k0, r, g, Hq, Hkv, G, nh, tid);
     }
+    const float sign = (pi / groups) ? 1.f : -1.f;
+    for (int u = wave; u < GS * NMT; u += 4)
+      score_unit<T, BLK, D, GS>(Ks, Qs, u / NMT, u % NMT, n16, j4, scale_log2, sign, colacc);
   }
 
   // Sum over the 16 query lanes of each lane group, then over the 4 waves.
@@ -155,19 +210,13 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(const float* __restri
   delta[idx] = s;
 }
 
-template <typename T, int BLK, int D>
+template <typename T, int BLK, int D, int GS>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
-  constexpr int ES = sizeof(T);
-  constexpr int ROW = D + 16 / ES;
-  const int G = a.Hq / a.Hkv;
-  // heads staged per pass: as many as fit in 96 KB of LDS, at most 4
-  int HS = G < 4 ? G : 4;
-  auto lds = [&](int hs) { return (size_t)(BLK + BLK * hs) * ROW * ES + 4 * BLK * sizeof(float); };
-  while (HS > 1 && lds(HS) > 96 * 1024) HS >>= 1;
-  const size_t shmem = lds(HS);
-  hipLaunchKernelGGL((score_partial_kernel<T, BLK, D>), dim3(a.B * a.Hkv), dim3(256), shmem, s,
-                     (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1, a.Hq, a.Hkv,
-                     HS, a.scale_log2, a.part);
+  constexpr int ROW = D + 16 / sizeof(T);
+  const size_t shmem = (size_t)BLK * (1 + GS) * ROW * sizeof(T) + 4 * BLK * sizeof(float);
+  hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS>), dim3(a.B * a.Hkv), dim3(256), shmem,
+                     s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1, a.Hq,
+                     a.Hkv, a.scale_log2, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(score_reduce_kernel, dim3((a.B * a.blk + 255) / 256), dim3(256), 0, s,
@@ -175,16 +224,30 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Heads staged per pass: as many of the G heads (at most 4) as keep one pass within ~54 KB of
+// LDS, so that three workgroups share a CU.
+template <typename T, int BLK, int D>
+hipError_t launch_g(const ScoreArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  constexpr size_t row = (size_t)(D + 16 / sizeof(T)) * sizeof(T);
+  constexpr size_t budget = 54 * 1024;
+  constexpr bool fit4 = (size_t)BLK * 5 * row <= budget;
+  constexpr bool fit2 = (size_t)BLK * 3 * row <= budget;
+  if (G >= 4 && fit4) return launch_t<T, BLK, D, 4>(a, s);
+  if (G >= 2 && fit2) return launch_t<T, BLK, D, 2>(a, s);
+  return launch_t<T, BLK, D, 1>(a, s);
+}
+
 template <typename T>
 hipError_t launch_dt(const ScoreArgs& a, hipStream_t s) {
   if (a.d == 64) {
-    if (a.blk == 16) return launch_t<T, 16, 64>(a, s);
-    if (a.blk == 32) return launch_t<T, 32, 64>(a, s);
-    return launch_t<T, 64, 64>(a, s);
+    if (a.blk == 16) return launch_g<T, 16, 64>(a, s);
+    if (a.blk == 32) return launch_g<T, 32, 64>(a, s);
+    return launch_g<T, 64, 64>(a, s);
   }
-  if (a.blk == 16) return launch_t<T, 16, 128>(a, s);
-  if (a.blk == 32) return launch_t<T, 32, 128>(a, s);
-  return launch_t<T, 64, 128>(a, s);
+  if (a.blk == 16) return launch_g<T, 16, 128>(a, s);
+  if (a.blk == 32) return launch_g<T, 32, 128>(a, s);
+  return launch_g<T, 64, 128>(a, s);
 }
 
 }  // namespace

@@ -298,3 +298,32 @@ def test_deterministic_bitwise():
     assert np.array_equal(a["delta"], b["delta"])
     assert np.array_equal(a["out_bits"], b["out_bits"])
     assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_attn_output_rounds_to_nearest_even():
+    # q = 0 gives every key weight exactly 1, so with 63 values of 1.0 and one of 1.75 over 64
+    # keys (32 prefix + 32 block) the f32 result is exactly 1 + 3/256, the midpoint between the
+    # bf16 neighbours 1 + 1/128 (odd mantissa) and 1 + 1/64 (even): nearest-even gives 1 + 1/64.
+    _announce("attn output rounding")
+    from workloads import f32_to_bf16_bits, pack_v
+    rec = BY_NAME["sdar_b32_blk32"].scaled(B=1)
+    st = make_step(rec, prefix_override=np.array([32]))
+    Hkv, d, S, blk = st.Hkv, st.d, st.S, st.blk
+    vals = np.ones((64, Hkv, d), dtype=np.float32)
+    vals[5] = 1.75                                          # one prefix key
+    vbits = f32_to_bf16_bits(vals)
+    pv = np.zeros((S, Hkv, d), dtype=np.uint16)
+    pv[:32] = vbits[:32]
+    st.v_cache[st.page_table[0, 0]] = pack_v(pv, S)[0]
+    st.v_blk[0] = pack_v(vbits[32:], blk)[0]
+    keep = np.zeros((1, blk), dtype=np.uint8)
+    keep[0, 3] = 1
+    c = attn_case_inputs(st, keep)
+    t = step_inputs(st)
+    dq = torch.zeros_like(c["d_q"])
+    out, lse = F.ragged_paged_attn(dq, c["d_offsets"], t.k_cache, t.v_cache, t.page_table,
+                                   t.prefix_len, t.k_blk, t.v_blk, 1, st.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.all(got == 1.0 + 1.0 / 64), np.unique(got)
+    assert np.allclose(lse.cpu().numpy(), np.log(64.0), atol=1e-6)
