@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--workload", default="sdar_b256_blk32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (known bytes) 5 times, "
+                         "to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md "
@@ -114,6 +117,21 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "ms": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
+        return
     from decodability_aware_token_amd import FocusStep, StepInputs
     from workloads import BY_NAME, make_step
     from workloads.torch_io import upload

@@ -94,10 +94,11 @@ def _stream(device: torch.device) -> int:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[Optional[torch.Tensor], int]:
+    """A caller's workspace, or a new zero-filled one (the attention needs zeros on first use)."""
     if nbytes == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 

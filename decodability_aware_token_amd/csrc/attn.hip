@@ -4,33 +4,52 @@
 // Bound", cards "Runtime Action" (ragged execution, intra-block KV caching) and "Motivation"
 // (block diffusion: the prefix is exactly KV-cached, the block attends bidirectionally).
 //
-// Work item = (request r, kv head g, query group, key split).  The G query heads of kv head g
-// are packed with the request's kept tokens into rows rho = t*G + hh (16 rows per MFMA tile,
-// QT tiles per item), so one pass over the KV serves every query head that reads it.
+// Work decomposition.  An item is (request r, kv head g, query group qg): the G query heads of
+// kv head g are packed with the request's kept tokens into rows rho = t*G + hh, 16*QT rows per
+// query group, so one pass over a head's KV serves all its query heads.  An item's keys are
+// streamed as 32-key tiles (columns), the prefix tiles first, then the block tiles.  The columns
+// of all requests form one global list.
 //
-// Each of the 4 waves streams its own 32-key tiles (tiles w, w+4, ... of the item) straight
-// from HBM into MFMA operand registers, double buffered:
-//   * K layout [page, Hkv, d/8, S, 8]: a lane's 16-byte load is 8 dims of one key, and the 16
-//     lanes of a quarter-wave read 4 runs of 4 consecutive keys (64 B each).  The tile is the
+// Column groups.  The grid holds as many waves as the GPU runs at once, in groups of Hkv*nqg
+// waves, one wave per (kv head, query group).  Group i takes the i-th of equal contiguous slices
+// of the column list, so the waves of a group stream the same pages of the same requests at the
+// same time, each its own kv head's part of the page: every page is read by all its heads
+// together, which keeps the DRAM accesses local wherever the slices fall.  A wave streams its
+// columns with the next tile's loads in flight while it computes the current one, crossing
+// request boundaries (page ids come from scalar loads that mostly hit the scalar cache; a new
+// item's queries are loaded as it starts).  A wave that holds a whole item writes its output
+// directly.  An item cut by slice boundaries has one piece per group it overlaps; the pieces
+// meet through an arrival counter: a piece that is not the last to finish stores its partial
+// (running max, sum, unnormalised O) and arrives; the last one merges every piece in key order
+// (its own from registers) and writes the output.  The piece at the end of a slice usually
+// finishes last, and sees that before storing anything.  Partials and counters use device-scope
+// atomic accesses, which stay coherent across the XCDs' separate L2 caches without an L2
+// write-back.  Every group does the same amount of streaming, so no wave waits for another.
+//
+// Register operands straight from HBM (no LDS):
+//   * K pages [page, Hkv, d/8, S, 8]: a lane's 16-byte load is 8 dims of one key; the tile is the
 //     A operand of S^T = K Q^T; key slot m of subtile s is key 8*(m/4) + 4*s + m%4, chosen so
 //     that the result lane group j holds exactly keys 8j..8j+7 of the tile.
-//   * V layout [page, Hkv, S/8, d, 8]: a lane's 16-byte load is one dim of 8 consecutive keys,
-//     which is exactly the A operand of O^T = V^T P^T for lane group j; a quarter-wave reads 256
-//     contiguous bytes.  P^T (bf16) comes straight from the S^T registers.
-// Softmax is online in the exp2 domain (f32).  The 4 waves merge (max, sum, O) in LDS in a fixed
-// order; items of long prefixes are split along the keys and merged by attn_combine_kernel, also
-// in a fixed order, so results are bitwise reproducible.
+//   * V pages [page, Hkv, S/8, d, 8]: a lane's 16-byte load is one dim of 8 consecutive keys,
+//     which is exactly the A operand of O^T = V^T P^T for lane group j (256 contiguous bytes per
+//     quarter-wave); P^T (bf16) comes straight from the S^T registers.
+// Softmax is online in the exp2 domain (f32).  Merges run in a fixed order, so results are
+// bitwise reproducible.
 #include "device_common.h"
 #include "launch.h"
 
 namespace focus {
 namespace {
 
-#ifndef FOCUS_ATTN_MAX_TILES_PER_SPLIT
-#define FOCUS_ATTN_MAX_TILES_PER_SPLIT 32
-#endif
-constexpr int kWaves = 4;
-constexpr int kMaxTilesPerSplit = FOCUS_ATTN_MAX_TILES_PER_SPLIT;  // 32-key tiles per work item
+constexpr int kWaves = 4;  // waves per workgroup
+// s_waitcnt immediate with vmcnt = 0 and the other counters at their maxima (GFX9 encoding):
+// waits until every vector memory access of the wave, stores included, has completed
+constexpr int kWaitVmcnt0 = 0x0F70;
+// cache-policy bits of a vector memory access with device scope (SC1): stores write through to
+// the device-coherent level, loads read from it (what device-scope atomics use on gfx950)
+constexpr int kCpolDevice = 16;
+// third word of a raw (unswizzled, 32-bit format) buffer resource
+constexpr int kRawBufferFormat = 0x00020000;
 
 struct Params {
   const uint16_t* q;
@@ -43,56 +62,120 @@ struct Params {
   const uint16_t* v_blk;
   uint16_t* out;
   float* lse;
-  float* ws_o;   // [slots][16*QT][D]
-  float* ws_ml;  // [slots][2][16*QT]   (max in log2 units, sum)
-  int cap, num_pages, max_pages, B, blk, Hq, Hkv, G, log2G, S, log2S, log2blk, max_kept;
-  int tiles_split, nsplit_max, nqg;
+  float* ws_o;     // [2W][QT][D/16][64 lanes][4] partial O (unnormalised), in register order
+  int ws_o_bytes;  // its size (the buffer-access range)
+  float* ws_ml;    // [2W][2][16*QT] partial running max (log2 units) and sum
+  int* counters;   // [W] arrivals per cut item, indexed by the item's first group and wave slot;
+                   // zero between calls (the last arrival resets it)
+  int cap, num_pages, max_pages, B, blk, Hq, Hkv, G, log2G, S, log2S, log2blk, max_kept, nqg;
+  int W;           // waves in the grid
+  int gs;          // waves per column group (Hkv * nqg)
+  int ngroups;     // column groups (W / gs; waves beyond ngroups * gs stay idle)
   float scale_log2;
 };
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 template <int D>
 struct Tile {
   u32x4_t k[2][D / 32];
   u32x4_t v[D / 16];
+  bool bad;  // a page id of the tile was out of range (page 0 was read instead)
 };
 
-// Loads tile `it` of the item's key sequence (prefix tiles first, then block tiles) into T.
-// Branch-free, so the compiler can keep the next tile's loads in flight (it counts them): each
-// lane's 8-key group is clamped to the group holding the segment's last valid key, which always
-// lies in an allocated page, and the keys past the valid length are masked in compute_tile.  An
-// out-of-range page id is replaced by page 0 and reported through `bad`.
+// Per-request metadata staged in LDS by every workgroup.
+struct Meta {
+  int* cum;   // [B+1] exclusive prefix sums of the requests' column counts
+  int* P;     // [B] prefix length, -1 if out of range (the request's rows become NaN)
+  int* off;   // [B] first compacted row
+  int* rows;  // [B] kept rows * G (0: request has no work)
+};
+
+// Position in the global column list (all fields wave-uniform).  Tile counts are derived from
+// the prefix length on demand to keep the scalar state small.  A wave's kv head and query group
+// never change.
+struct Cursor {
+  int r, g, qg, tt;  // request, kv head, query group, tile within the item
+  int P;             // prefix length of r, -1 if out of range (the item's rows become NaN)
+  int off0, nrows;   // first compacted row of r, its kept rows * G
+  int start;         // global index of the request's first column
+  __device__ __forceinline__ int plen() const { return P < 0 ? 0 : P; }
+  __device__ __forceinline__ int ntp() const { return (plen() + 31) >> 5; }
+};
+
+__device__ __forceinline__ int item_tiles(const Cursor& c, const Params& p) {
+  return c.ntp() + ((p.blk + 31) >> 5);
+}
+
+__device__ __forceinline__ void set_request(Cursor& c, int r, const Meta& m) {
+  c.r = r;
+  c.P = uni(m.P[r]);
+  c.off0 = uni(m.off[r]);
+  c.nrows = uni(m.rows[r]);
+}
+
+__device__ __forceinline__ void advance(Cursor& c, const Meta& m, const Params& p) {
+  const int nt = item_tiles(c, p);
+  if (++c.tt < nt) return;
+  c.start += nt;
+  c.tt = 0;
+  int r = c.r + 1;
+  while (r < p.B - 1 && uni(m.cum[r + 1]) == uni(m.cum[r])) ++r;
+  set_request(c, r, m);
+}
+
+// Page ids of the (at most two) pages a prefix tile touches, as scalar loads (consecutive tiles
+// share the page table's cache lines).
+struct Pages {
+  int a, b;
+};
+__device__ __forceinline__ Pages fetch_pages(const Cursor& c, const Params& p,
+                                             const int32_t* __restrict__ page_table) {
+  Pages pg{0, 0};
+  if (c.tt < c.ntp()) {
+    const int p0 = (c.tt * 32) >> p.log2S;
+    const int last = (c.plen() - 1) >> p.log2S;
+    const int32_t* row = page_table + (size_t)c.r * p.max_pages;
+    pg.a = row[p0];
+    pg.b = row[min(p0 + 1, last)];
+  }
+  return pg;
+}
+
+// Loads the cursor's tile.  Branch-free: each lane's 8-key group is clamped to the group of the
+// segment's last valid key, which lies in an allocated page; keys past the valid length are
+// masked in compute_tile.  An out-of-range page id is replaced by page 0 and reported in T.bad.
 template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& T, const Params& p, int it, int ntp, int P,
-                                          int r, int g, const int* s_pages, int pg0, int lane,
-                                          bool& bad) {
+__device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg, const Params& p,
+                                          int lane) {
   constexpr int NK = D / 32, ND = D / 16;
   const int m16 = lane & 15, j4 = lane >> 4;
-  const bool paged = it < ntp;  // wave-uniform
-  const int key0 = paged ? it * 32 : (it - ntp) * 32;
-  const int nvalid = paged ? P : p.blk;
+  const int ntp = c.ntp();
+  const bool paged = c.tt < ntp;
+  const int key0 = paged ? c.tt * 32 : (c.tt - ntp) * 32;
+  const int nvalid = paged ? c.plen() : p.blk;
   const int log2S = paged ? p.log2S : p.log2blk;
   const int S = 1 << log2S;
   const size_t page_elems = (size_t)D << log2S;  // one (page, kv head) block
   const int last_group = (nvalid - 1) & ~7;
-
-  // K: keys kg + (m16 & 3) + 4*s of the lane's 8-key group kg (s = 0, 1: the two subtiles)
   const int kg = min(key0 + 8 * (m16 >> 2), last_group);
-  // V: the 8 keys vg .. vg+7 of lane group j4
   const int vg = min(key0 + 8 * j4, last_group);
   const uint16_t* kbase;
   const uint16_t* vbase;
   if (paged) {
-    int pk = s_pages[(kg >> log2S) - pg0];
-    int pv = s_pages[(vg >> log2S) - pg0];
+    const int p0 = key0 >> log2S;
+    int pk = ((kg >> log2S) == p0) ? pg.a : pg.b;
+    int pv = ((vg >> log2S) == p0) ? pg.a : pg.b;
     const bool okk = pk >= 0 && pk < p.num_pages, okv = pv >= 0 && pv < p.num_pages;
-    bad = bad || !okk || !okv;
+    T.bad = !okk || !okv;
     pk = okk ? pk : 0;
     pv = okv ? pv : 0;
-    kbase = p.k_cache + ((size_t)pk * p.Hkv + g) * page_elems;
-    vbase = p.v_cache + ((size_t)pv * p.Hkv + g) * page_elems;
+    kbase = p.k_cache + ((size_t)pk * p.Hkv + c.g) * page_elems;
+    vbase = p.v_cache + ((size_t)pv * p.Hkv + c.g) * page_elems;
   } else {
-    kbase = p.k_blk + ((size_t)r * p.Hkv + g) * page_elems;
-    vbase = p.v_blk + ((size_t)r * p.Hkv + g) * page_elems;
+    T.bad = false;
+    kbase = p.k_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
+    vbase = p.v_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
   }
   const int kslot = (kg & (S - 1)) + (m16 & 3);
   const uint16_t* kp = kbase + ((size_t)((j4 << log2S) + kslot) << 3);
@@ -104,6 +187,24 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Params& p, int it, i
   const uint16_t* vp = vbase + ((size_t)((vg & (S - 1)) >> 3) * D + m16) * 8;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) T.v[dt] = load16v(vp + 16 * dt * 8);
+}
+
+// Loads the B operand (Q^T) of the cursor's item.  Rows past the item's rows (or past cap) are
+// clamped to a valid row: their results are never written, and finite inputs keep them finite.
+template <int D, int QT>
+__device__ __forceinline__ void load_q(u32x4_t (&qf)[QT][D / 32], const Cursor& c,
+                                       const Params& p, int lane) {
+  constexpr int NK = D / 32, R = 16 * QT;
+  const int m16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int rho = min(c.qg * R + 16 * qt + m16, c.nrows - 1);
+    const int tok = min(c.off0 + (rho >> p.log2G), p.cap - 1);
+    const uint16_t* qrow =
+        p.q + ((size_t)tok * p.Hq + c.g * p.G + (rho & (p.G - 1))) * D + 8 * j4;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qf[qt][kk] = load16v(qrow + 32 * kk);
+  }
 }
 
 template <int D, int QT>
@@ -170,212 +271,328 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
   }
 }
 
+// Column group whose slice holds column t: the largest i with floor(i*T/n) <= t.
+__device__ __forceinline__ int group_of(int t, int total, int n) {
+  return (int)(((long long)(t + 1) * n - 1) / total);
+}
+__device__ __forceinline__ int slice_begin(int i, int total, int n) {
+  return (int)(((long long)i * total) / n);
+}
+
+// page_table is a separate restrict argument so that its (uniform) reads become scalar loads.
 template <int D, int QT>
-__global__ __launch_bounds__(256, (QT >= 4 ? 1 : 2)) void attn_kernel(Params p) {
+__global__ __launch_bounds__(256, (QT >= 2 ? 1 : 2)) void attn_kernel(
+    Params p, const int32_t* __restrict__ page_table) {
   constexpr int NK = D / 32, ND = D / 16, R = 16 * QT;
-  constexpr int OROW = D + 4;  // padded LDS row (floats)
-  constexpr int MAXPG = kMaxTilesPerSplit * 32 / 16 + 2;
-  __shared__ __align__(16) float s_o[kWaves][16][OROW];
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ int s_pages[MAXPG];
-  __shared__ int s_bad;
-
+  extern __shared__ __align__(16) int smem_i[];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = uni(tid >> 6);
   const int m16 = lane & 15, j4 = lane >> 4;
-  const int BH = p.B * p.Hkv;
-  const int rg = blockIdx.x % BH, split = blockIdx.x / BH;
-  const int r = rg / p.Hkv, g = rg % p.Hkv;
-  const int qg = blockIdx.y;
+  const int B = p.B;
 
-  const int off0 = p.offsets[r], off1 = p.offsets[r + 1];
-  const int kr = min(off1 - off0, p.max_kept);
-  if (off0 < 0 || kr <= 0 || off0 >= p.cap) return;
-  const int nrows = kr << p.log2G;
-  const int row0 = qg * R;
-  if (row0 >= nrows) return;
-  int P = p.prefix_len[r];
-  const bool bad_len = P < 0 || P > (p.max_pages << p.log2S);
-  if (bad_len) P = 0;
-  const int ntp = (P + 31) >> 5;
-  const int nt = ntp + ((p.blk + 31) >> 5);
-  const int nsplit = (nt + p.tiles_split - 1) / p.tiles_split;
-  if (split >= nsplit) return;
-  const int t0 = split * p.tiles_split;
-  const int t1 = min(nt, t0 + p.tiles_split);
-
-  // this split's page ids
-  int pg0 = 0;
-  if (tid == 0) s_bad = bad_len ? 1 : 0;
-  if (t0 < ntp) {
-    pg0 = (t0 * 32) >> p.log2S;
-    const int pg1 = min((P - 1) >> p.log2S, ((min(t1, ntp) * 32 - 1) >> p.log2S)) + 1;
-    for (int i = tid; i < pg1 - pg0; i += 256)
-      s_pages[i] = p.page_table[(size_t)r * p.max_pages + pg0 + i];
+  // ---- stage the requests' metadata and tile counts in LDS (every workgroup does this)
+  Meta meta;
+  meta.cum = smem_i;
+  meta.P = smem_i + (B + 1);
+  meta.off = meta.P + B;
+  meta.rows = meta.off + B;
+  int* s_part = meta.rows + B;  // [256]
+  const int per = (B + 255) / 256;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int r = tid * per + i;
+    if (r >= B) break;
+    const int off0 = p.offsets[r], off1 = p.offsets[r + 1];
+    int P = p.prefix_len[r];
+    const int kr = min(off1 - off0, p.max_kept);
+    const bool has = off0 >= 0 && kr > 0 && off0 < p.cap;
+    const int nrows = has ? kr << p.log2G : 0;
+    const bool badP = P < 0 || P > (p.max_pages << p.log2S);
+    meta.P[r] = badP ? -1 : P;
+    meta.off[r] = off0;
+    meta.rows[r] = nrows;
+    if (badP) P = 0;
+    const int nt = ((P + 31) >> 5) + ((p.blk + 31) >> 5);
+    const int tiles = has ? nt : 0;
+    meta.cum[r + 1] = tiles;
+    local += tiles;
+  }
+  s_part[tid] = local;
+  __syncthreads();
+  if (tid < 64) {  // exclusive scan of the 256 partial sums by wave 0
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = s_part[4 * tid + i];
+      s += v[i];
+    }
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    int run = incl - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_part[4 * tid + i] = run;
+      run += v[i];
+    }
+  }
+  __syncthreads();
+  {
+    int run = s_part[tid];
+    for (int i = 0; i < per; ++i) {
+      const int r = tid * per + i;
+      if (r >= B) break;
+      run += meta.cum[r + 1];
+      meta.cum[r + 1] = run;
+    }
+    if (tid == 0) meta.cum[0] = 0;
   }
   __syncthreads();
 
-  // queries of this item (B operand): lane (n = m16, j4) row rho = row0 + 16*qt + n
-  u32x4_t qf[QT][NK];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int rho = row0 + 16 * qt + m16;
-    const int tok = off0 + (rho >> p.log2G);
-    const bool valid = rho < nrows && tok < p.cap;
-    const uint16_t* qrow =
-        p.q + ((size_t)tok * p.Hq + g * p.G + (rho & (p.G - 1))) * D;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      qf[qt][kk] = valid ? load16v(qrow + (4 * kk + j4) * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  // ---- this wave's group, and the group's slice [a, b) of the global column list
+  const int total = uni(meta.cum[B]);
+  const int w = blockIdx.x * kWaves + wave;
+  const int gi = w / p.gs, hi = w - gi * p.gs;
+  const int a = slice_begin(gi, total, p.ngroups);
+  const int b = slice_begin(gi + 1, total, p.ngroups);
+  if (gi >= p.ngroups || a >= b) return;
+
+  // largest r with cum[r] <= col (requests without columns are skipped by the search)
+  auto locate = [&](int col) {
+    int lo = 0, hi_r = B;
+    while (hi_r - lo > 1) {
+      const int mid = (lo + hi_r) >> 1;
+      if (uni(meta.cum[mid]) <= col)
+        lo = mid;
+      else
+        hi_r = mid;
+    }
+    return lo;
+  };
+  // The slice is processed rotated: first [x, b), where x is the start of the request holding
+  // the slice's last column (or a), then [a, x).  So both pieces that may be cut at the slice
+  // boundaries come first and their merges happen while the other waves still stream, instead
+  // of at the end of the kernel.
+  Cursor Ca;
+  {
+    const int r = locate(a);
+    set_request(Ca, r, meta);
+    Ca.g = hi / p.nqg;
+    Ca.qg = hi - Ca.g * p.nqg;
+    Ca.start = uni(meta.cum[r]);
+    Ca.tt = a - Ca.start;
   }
+  Cursor C = Ca;
+  int x = a;
+  {
+    const int r = locate(b - 1);
+    const int sb = uni(meta.cum[r]);
+    if (sb > a) {
+      x = sb;
+      set_request(C, r, meta);
+      C.start = sb;
+      C.tt = 0;
+    }
+  }
+  const int n = b - a, n1 = b - x;  // tiles in the slice, in the first segment
 
   f32x4_t o[QT][ND];
   float mrun[QT], lrun[QT];
+  auto reset = [&]() {
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = -INFINITY;
-    lrun[qt] = 0.f;
+    for (int qt = 0; qt < QT; ++qt) {
+      mrun[qt] = -INFINITY;
+      lrun[qt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+      for (int dt = 0; dt < ND; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  reset();
 
-  // Each wave streams tiles wave, wave+4, ... of [t0, t1), loading tile k+1 while it computes
-  // tile k.  The prefetch is unconditional (after the wave's last tile it re-reads that tile, a
-  // cache hit), so the wait before each compute only drains the older tile's loads.
+  // Writes the finished piece of item c: the output itself if the slice holds the whole item,
+  // else the piece takes part in the item's arrival protocol.
+  auto finalize = [&](const Cursor& c, bool piece_bad) {
+    float lt[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      lt[qt] = wave_sum_xor(lrun[qt], 16);
+      lt[qt] = wave_sum_xor(lt[qt], 32);
+    }
+    const int end = c.start + item_tiles(c, p);
+    // a bad page id seen by any lane taints every row (the products mix all lanes)
+    const bool nan_out = __ballot(piece_bad) != 0 || c.P < 0;
+    auto write_out = [&](int qt, const f32x4_t (&acc)[ND], float m, float l) {
+      const int rho = c.qg * R + 16 * qt + m16;
+      const int tok = c.off0 + (rho >> p.log2G);
+      if (rho < c.nrows && tok < p.cap) {
+        const int h = c.g * p.G + (rho & (p.G - 1));
+        const float inv = nan_out ? __builtin_nanf("") : 1.f / l;
+        uint16_t* orow = p.out + ((size_t)tok * p.Hq + h) * D + 4 * j4;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          uint2 w2;
+          w2.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+          w2.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+          *reinterpret_cast<uint2*>(orow + 16 * dt) = w2;
+        }
+        if (j4 == 0 && p.lse != nullptr)
+          p.lse[(size_t)tok * p.Hq + h] = nan_out ? __builtin_nanf("") : (m + __log2f(l)) * kLn2;
+      }
+    };
+    if (a <= c.start && end <= b) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) write_out(qt, o[qt], mrun[qt], lt[qt]);
+      return;
+    }
+    if (c.qg * R >= c.nrows) return;  // the request has no rows in this query group
+    // pieces of the item in key order: the group holding the item's first column, then the
+    // groups whose slices start inside it; the counter belongs to the first group's wave slot
+    const int gf = group_of(c.start, total, p.ngroups);
+    int* counter = p.counters + gf * p.gs + hi;
+    int npieces = 0;
+    for (int tp = c.start; tp < end; tp = slice_begin(group_of(tp, total, p.ngroups) + 1, total,
+                                                       p.ngroups))
+      ++npieces;
+    const int own_slot = a > c.start ? 2 * w : 2 * w + 1;
+    // partial O through buffer accesses with device scope (write-through, coherent reads): each
+    // instruction moves 1 KiB of one (slot, query tile, 16-dim block) in lane order
+    const __amdgpu_buffer_rsrc_t rs_o =
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_o, 0, p.ws_o_bytes, kRawBufferFormat);
+    auto o_off = [&](int slot, int qt, int dt) {
+      return (((slot * QT + qt) * ND + dt) * 64 + lane) * 16;
+    };
+    int seen = 0;
+    if (lane == 0) seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool last = uni(seen) == npieces - 1;
+    if (!last) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int row = 16 * qt + m16;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[qt][dt]), rs_o,
+                                                 o_off(own_slot, qt, dt), 0, kCpolDevice);
+        if (j4 == 0) {
+          __hip_atomic_store(p.ws_ml + ((size_t)own_slot * 2) * R + row, mrun[qt],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(p.ws_ml + ((size_t)own_slot * 2 + 1) * R + row,
+                             nan_out ? __builtin_nanf("") : lt[qt], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      // the partial must be complete at device scope before the arrival is counted
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      int old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = uni(old) == npieces - 1;
+    }
+    if (!last) return;
+    // last arrival: merge every piece in key order (own piece from registers), then reset the
+    // counter for the next call
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int row = 16 * qt + m16;
+      float M = -INFINITY;
+      for (int tp = c.start; tp < end;) {
+        const int gv = group_of(tp, total, p.ngroups);
+        const int sl = tp == c.start ? 2 * (gv * p.gs + hi) + 1 : 2 * (gv * p.gs + hi);
+        tp = slice_begin(gv + 1, total, p.ngroups);
+        const float ms = sl == own_slot ? mrun[qt]
+                                        : __hip_atomic_load(p.ws_ml + ((size_t)sl * 2) * R + row,
+                                                            __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+        M = fmaxf(M, ms);
+      }
+      float L = 0.f;
+      f32x4_t acc[ND];
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int tp = c.start; tp < end;) {
+        const int gv = group_of(tp, total, p.ngroups);
+        const int sl = tp == c.start ? 2 * (gv * p.gs + hi) + 1 : 2 * (gv * p.gs + hi);
+        tp = slice_begin(gv + 1, total, p.ngroups);
+        // the same operations whether a piece comes from registers or from memory, so the
+        // result does not depend on which piece arrived last
+        const bool own = sl == own_slot;
+        float ms, ls;
+        if (own) {
+          ms = mrun[qt];
+          ls = nan_out ? __builtin_nanf("") : lt[qt];
+        } else {
+          ms = __hip_atomic_load(p.ws_ml + ((size_t)sl * 2) * R + row, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+          ls = __hip_atomic_load(p.ws_ml + ((size_t)sl * 2 + 1) * R + row, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const float sc = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+        L = __builtin_fmaf(ls, sc, L);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          const f32x4_t v =
+              own ? o[qt][dt]
+                  : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rs_o, o_off(sl, qt, dt), 0, kCpolDevice));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[dt][i] = __builtin_fmaf(v[i], sc, acc[dt][i]);
+        }
+      }
+      write_out(qt, acc, M, L);
+    }
+    if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // ---- stream: compute tile tv (cursor C, buffer X) while tile tv+1 (cursor L, buffer Y) is
+  // in flight; tv counts tiles in processing order.  Past the slice end L stays on the last
+  // tile, so the prefetch is unconditional (it re-reads that tile: cache hits).  When C starts a
+  // piece its queries are loaded before Y's tile, so the compute's wait does not drain Y.
+  u32x4_t qf[QT][NK];
+  load_q<D, QT>(qf, C, p, lane);
+  Cursor L = C;
+  int tvl = 0;  // processing index of L
+  auto step_l = [&]() {
+    if (tvl + 1 == n1)
+      L = Ca;
+    else
+      advance(L, meta, p);
+    ++tvl;
+  };
+  if (n > 1) step_l();
   bool bad = false;
   Tile<D> ta, tb;
-  const int nk = t0 + wave < t1 ? (t1 - t0 - wave + kWaves - 1) / kWaves : 0;
-  auto tile_of = [&](int k) { return t0 + wave + kWaves * min(k, nk - 1); };
-  static_assert(kMaxTilesPerSplit % (2 * kWaves) == 0, "tile loop unrolls by two buffers");
-  auto seg_key0 = [&](int i) { return i < ntp ? i * 32 : (i - ntp) * 32; };
-  auto seg_len = [&](int i) { return i < ntp ? P : p.blk; };
-  if (nk > 0) {
-    // fully unrolled (a wave takes at most kMaxTilesPerSplit / kWaves tiles of a split), so the
-    // code is straight-line and the buffers alternate statically
-    load_tile<D>(ta, p, tile_of(0), ntp, P, r, g, s_pages, pg0, lane, bad);
-#pragma unroll
-    for (int k = 0; k < kMaxTilesPerSplit / kWaves; k += 2) {
-      load_tile<D>(tb, p, tile_of(k + 1), ntp, P, r, g, s_pages, pg0, lane, bad);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      int it = tile_of(k);
-      compute_tile<D, QT>(ta, seg_key0(it), seg_len(it), qf, o, mrun, lrun, p.scale_log2, lane);
-      if (k + 1 >= nk) break;
-      load_tile<D>(ta, p, tile_of(k + 2), ntp, P, r, g, s_pages, pg0, lane, bad);
-      __builtin_amdgcn_sched_barrier(0);
-      it = tile_of(k + 1);
-      compute_tile<D, QT>(tb, seg_key0(it), seg_len(it), qf, o, mrun, lrun, p.scale_log2, lane);
-      if (k + 2 >= nk) break;
-    }
-  }
+  load_tile<D>(ta, C, fetch_pages(C, p, page_table), p, lane);
+  int tv = 0;
 
-  // Merge the 4 waves (fixed order), one 16-row query tile at a time, and write the result or
-  // this split's partial.
-  const int slot = (rg * p.nsplit_max + split) * p.nqg + qg;
-  constexpr int C4 = D / 4;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    // per-wave totals: the 4 lane groups hold disjoint keys' partial sums
-    float lt = wave_sum_xor(lrun[qt], 16);
-    lt = wave_sum_xor(lt, 32);
-    if (qt > 0) __syncthreads();  // the previous tile's readers are done
-    if (j4 == 0) {
-      s_m[wave][m16] = mrun[qt];
-      s_l[wave][m16] = lt;
-    }
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-      *reinterpret_cast<f32x4_t*>(&s_o[wave][m16][16 * dt + 4 * j4]) = o[qt][dt];
-    if (bad) s_bad = 1;
-    __syncthreads();
-    const bool isbad = s_bad != 0;
-    for (int item = tid; item < 16 * C4; item += 256) {
-      const int rl = item / C4, c4 = item % C4;
-      const int row = 16 * qt + rl;
-      float M = s_m[0][rl];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][rl]);
-      float L = 0.f;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float sc = s_m[w][rl] == -INFINITY ? 0.f : fast_exp2(s_m[w][rl] - M);
-        L += s_l[w][rl] * sc;
-        acc += *reinterpret_cast<const f32x4_t*>(&s_o[w][rl][4 * c4]) * sc;
-      }
-      const int rho = row0 + row;
-      if (nsplit == 1) {
-        const int tok = off0 + (rho >> p.log2G);
-        if (rho >= nrows || tok >= p.cap) continue;
-        const int h = g * p.G + (rho & (p.G - 1));
-        const float inv = isbad ? __builtin_nanf("") : 1.f / L;
-        uint2 w2;
-        w2.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        w2.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-        *reinterpret_cast<uint2*>(p.out + ((size_t)tok * p.Hq + h) * D + 4 * c4) = w2;
-        if (c4 == 0 && p.lse != nullptr)
-          p.lse[(size_t)tok * p.Hq + h] = isbad ? __builtin_nanf("") : (M + __log2f(L)) * kLn2;
-      } else {
-        if (isbad) {
-          acc = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                        __builtin_nanf("")};
-          L = __builtin_nanf("");
-        }
-        *reinterpret_cast<f32x4_t*>(p.ws_o + ((size_t)slot * R + row) * D + 4 * c4) = acc;
-        if (c4 == 0) {
-          p.ws_ml[((size_t)slot * 2) * R + row] = M;
-          p.ws_ml[((size_t)slot * 2 + 1) * R + row] = L;
-        }
+  // A step past the slice end only issues its (cache-hitting) prefetch, so that the loop has a
+  // single exit, after every second step: an exit between the two buffer roles would let the
+  // compiler merge the two roles' pending loads at the loop head and drain the prefetch there.
+  auto step = [&](Tile<D>& X, Tile<D>& Y) {
+    const bool live = tv < n;
+    if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
+    load_tile<D>(Y, L, fetch_pages(L, p, page_table), p, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+    if (live) {
+      const int ntp = C.ntp();
+      const bool pg = C.tt < ntp;
+      compute_tile<D, QT>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk, qf, o,
+                          mrun, lrun, p.scale_log2, lane);
+      bad = bad || X.bad;
+      if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
+        finalize(C, bad);
+        reset();
+        bad = false;
       }
     }
-  }
-}
-
-// Merges the key splits of every (request, kv head, query group) with more than one split.
-template <int D, int QT>
-__global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
-  constexpr int R = 16 * QT, C4 = D / 4;
-  const int tid = threadIdx.x;
-  const int rg = blockIdx.x, qg = blockIdx.y;
-  const int r = rg / p.Hkv, g = rg % p.Hkv;
-  const int off0 = p.offsets[r], off1 = p.offsets[r + 1];
-  const int kr = min(off1 - off0, p.max_kept);
-  if (off0 < 0 || kr <= 0 || off0 >= p.cap) return;
-  const int nrows = kr << p.log2G;
-  const int row0 = qg * R;
-  if (row0 >= nrows) return;
-  int P = p.prefix_len[r];
-  if (P < 0 || P > (p.max_pages << p.log2S)) P = 0;
-  const int nt = ((P + 31) >> 5) + ((p.blk + 31) >> 5);
-  const int nsplit = (nt + p.tiles_split - 1) / p.tiles_split;
-  if (nsplit <= 1) return;
-  for (int item = tid; item < R * C4; item += 256) {
-    const int row = item / C4, c4 = item % C4;
-    const int rho = row0 + row;
-    const int tok = off0 + (rho >> p.log2G);
-    if (rho >= nrows || tok >= p.cap) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) {
-      const int slot = (rg * p.nsplit_max + s) * p.nqg + qg;
-      M = fmaxf(M, p.ws_ml[((size_t)slot * 2) * R + row]);
-    }
-    float L = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const int slot = (rg * p.nsplit_max + s) * p.nqg + qg;
-      const float ms = p.ws_ml[((size_t)slot * 2) * R + row];
-      const float sc = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-      L += p.ws_ml[((size_t)slot * 2 + 1) * R + row] * sc;
-      acc += *reinterpret_cast<const f32x4_t*>(p.ws_o + ((size_t)slot * R + row) * D + 4 * c4) *
-             sc;
-    }
-    const int h = g * p.G + (rho & (p.G - 1));
-    const float inv = 1.f / L;
-    uint2 w2;
-    w2.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    w2.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<uint2*>(p.out + ((size_t)tok * p.Hq + h) * D + 4 * c4) = w2;
-    if (c4 == 0 && p.lse != nullptr) p.lse[(size_t)tok * p.Hq + h] = (M + __log2f(L)) * kLn2;
+    C = L;
+    if (tvl + 1 < n) step_l();
+    ++tv;
+  };
+  while (true) {
+    step(ta, tb);
+    step(tb, ta);
+    if (tv >= n) break;
   }
 }
 
@@ -385,14 +602,25 @@ int ilog2(int x) {
   return l;
 }
 
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, int QT>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
-  dim3 grid(prm.B * prm.Hkv * plan.nsplit_max, plan.nqg);
-  hipLaunchKernelGGL((attn_kernel<D, QT>), grid, dim3(256), 0, s, prm);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.nsplit_max <= 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<D, QT>), dim3(prm.B * prm.Hkv, plan.nqg), dim3(256), 0,
-                     s, prm);
+  const size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
+  hipLaunchKernelGGL((attn_kernel<D, QT>), dim3(plan.wgs), dim3(256), shmem, s, prm,
+                     prm.page_table);
   return hipGetLastError();
 }
 
@@ -404,19 +632,19 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
   const int rows = max_kept * G;
   pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
+  // as many 4-wave workgroups as the GPU holds at once: 2 waves per SIMD with one query tile
+  // (registers <= 256), else 1 wave per SIMD
+  pl.wgs = device_cus() * (pl.qt == 1 ? 2 : 1);
   const long long ntiles_max = ((long long)max_pages * S + 31) / 32 + (blk + 31) / 32;
-  // Split the keys so that even a batch of maximal prefixes offers ~2048 work items.
-  int ts = kMaxTilesPerSplit;
-  while (ts > 8 && (long long)B * Hkv * pl.nqg * ((ntiles_max + ts - 1) / ts) < 2048) ts >>= 1;
-  pl.tiles_split = ts;
-  pl.nsplit_max = (int)((ntiles_max + ts - 1) / ts);
-  if (pl.nsplit_max > 1) {
-    const size_t slots = (size_t)B * Hkv * pl.nsplit_max * pl.nqg;
-    const size_t R = 16 * (size_t)pl.qt;
-    pl.ws_bytes = slots * R * (size_t)d * sizeof(float) + slots * 2 * R * sizeof(float);
-  } else {
-    pl.ws_bytes = 0;
-  }
+  pl.tiles_bound = (long long)B * ntiles_max;
+  pl.gs = Hkv * pl.nqg;
+  pl.ngroups = pl.wgs * kWaves / pl.gs;
+  const size_t W = (size_t)pl.wgs * kWaves;
+  const size_t R = 16 * (size_t)pl.qt;
+  pl.cnt_bytes = (W * sizeof(int) + 255) & ~(size_t)255;  // arrival counters
+  pl.ws_o_bytes = 2 * W * R * (size_t)d * sizeof(float);
+  pl.ws_ml_bytes = 2 * W * 2 * R * sizeof(float);
+  pl.ws_bytes = pl.cnt_bytes + pl.ws_o_bytes + pl.ws_ml_bytes;
   return pl;
 }
 
@@ -445,16 +673,16 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
   prm.log2S = ilog2(a.S);
   prm.log2blk = ilog2(a.blk);
   prm.max_kept = a.max_kept;
-  prm.tiles_split = plan.tiles_split;
-  prm.nsplit_max = plan.nsplit_max;
   prm.nqg = plan.nqg;
+  prm.W = plan.wgs * kWaves;
+  prm.gs = plan.gs;
+  prm.ngroups = plan.ngroups;
   prm.scale_log2 = a.scale_log2;
-  if (plan.nsplit_max > 1) {
-    const size_t slots = (size_t)a.B * a.Hkv * plan.nsplit_max * plan.nqg;
-    const size_t R = 16 * (size_t)plan.qt;
-    prm.ws_o = reinterpret_cast<float*>(a.workspace);
-    prm.ws_ml = prm.ws_o + slots * R * a.d;
-  }
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  prm.counters = reinterpret_cast<int*>(ws);
+  prm.ws_o = reinterpret_cast<float*>(ws + plan.cnt_bytes);
+  prm.ws_o_bytes = (int)plan.ws_o_bytes;
+  prm.ws_ml = reinterpret_cast<float*>(ws + plan.cnt_bytes + plan.ws_o_bytes);
   if (a.d == 64) {
     if (plan.qt == 1) return launch_dq<64, 1>(prm, plan, s);
     if (plan.qt == 2) return launch_dq<64, 2>(prm, plan, s);

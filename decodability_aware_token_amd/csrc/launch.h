@@ -67,11 +67,16 @@ struct AttnArgs {
   void* workspace;
 };
 struct AttnPlan {
-  int qt;           // 16-row query tiles per work item (1, 2 or 4)
-  int nqg;          // query groups per (request, kv head)
-  int tiles_split;  // 32-key tiles per split (multiple of 4)
-  int nsplit_max;   // splits per (request, kv head) at the longest possible prefix
-  size_t ws_bytes;  // partial-result workspace
+  int qt;                // 16-row query tiles per work item (1, 2 or 4)
+  int nqg;               // query groups per (request, kv head) at max_kept
+  int wgs;               // persistent workgroups (4 waves each)
+  int gs;                // waves per column group: one per (kv head, query group)
+  int ngroups;           // column groups in the grid (0: Hkv * nqg exceeds the grid)
+  long long tiles_bound; // 32-key columns of all requests at the longest possible prefixes
+  size_t cnt_bytes;      // arrival counters of cut items (zero between calls)
+  size_t ws_o_bytes;     // partial outputs of items cut by slice boundaries
+  size_t ws_ml_bytes;    // their running max / sum
+  size_t ws_bytes;       // total workspace
 };
 AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);

@@ -61,7 +61,7 @@ class FocusStep:
         self.ws_score = torch.empty(max(nsc, 1), dtype=torch.uint8, device=dev)
         S = inp.k_cache.shape[3]
         nat = F.attn_workspace_bytes(B, blk, Hq, Hkv, d, S, inp.page_table.shape[1], inp.max_kept)
-        self.ws_attn = torch.empty(max(nat, 1), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.zeros(max(nat, 1), dtype=torch.uint8, device=dev)  # zeros once
 
     def score(self):
         i = self.inp

@@ -64,7 +64,7 @@ int focus_version(void);
  *   workspace   device scratch of at least focus_score_l01_workspace_size(...) bytes
  *               (may be NULL when that size is 0); contents need no initialisation
  * Supported: blk in {16,32,64}; d in {64,128}; Hq % Hkv == 0; Hq/Hkv in {1,2,4,8};
- *            1 <= B <= 65535; Hkv <= 64.  Pointers must be 16-byte aligned.
+ *            1 <= B <= 4096; Hkv <= 64.  Pointers must be 16-byte aligned.
  * ------------------------------------------------------------------------------------------ */
 size_t focus_score_l01_workspace_size(int B, int blk, int Hq, int Hkv, int d);
 int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* k1, int dtype,
@@ -86,7 +86,7 @@ int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* 
  *
  *   delta       [B, blk] f32         masked [B, blk] u8      budget [B] i32 (ignored if adaptive)
  *   keep        [B, blk] u8 output (1 = kept)                kept_count [B] i32 output
- * Supported: blk in {16,32,64}; 1 <= B <= 2^24.
+ * Supported: blk in {16,32,64}; 1 <= B <= 4096.
  * ------------------------------------------------------------------------------------------ */
 int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t* budget,
                         int adaptive, float beta, int lo, int hi, int B, int blk, uint8_t* keep,
@@ -109,8 +109,8 @@ int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t
  *   rows        [B, blk, row_bytes] bytes, or NULL (then gathered must be NULL: offsets only)
  *   offsets     [B+1] i32 output        kept_pos [cap] i32 output (may be NULL)
  *   gathered    [cap, row_bytes] output, or NULL
- * Supported: blk in {16,32,64}; 1 <= B <= 2^20; row_bytes > 0 and a multiple of 16; rows and
- *            gathered 16-byte aligned.
+ * Supported: blk in {16,32,64}; 1 <= B <= 4096; row_bytes > 0 and a multiple of 16; rows and
+ *            gathered 16-byte aligned; keep 4-byte aligned.
  * ------------------------------------------------------------------------------------------ */
 int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
                   int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,
@@ -140,9 +140,14 @@ int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t
  * written.  Device data the host cannot check: a request whose prefix_len is negative or above
  * max_pages*S, or whose used page ids fall outside [0, num_pages), gets NaN in all its output
  * rows instead of a memory access.
- *   workspace   at least focus_ragged_paged_attn_workspace_size(...) bytes, no initialisation
+ *   workspace   at least focus_ragged_paged_attn_workspace_size(...) bytes, ZERO-FILLED before its
+ *               first use (it holds arrival counters that every call leaves at zero again, plus
+ *               per-wave partial results); calls that share a workspace must not run
+ *               concurrently.  The size depends on the current device's compute-unit count.
  * Supported: d in {64,128}; S in {16,32,64}; blk in {16,32,64}; Hq/Hkv in {1,2,4,8};
- *            1 <= max_kept <= blk; 1 <= B <= 65535; pointers 16-byte aligned.
+ *            1 <= max_kept <= blk; 1 <= B <= 4096; max_pages*S <= 2^24; fewer than 2^31 key
+ *            tiles of 32 over all (request, kv head, query group) at the longest prefixes;
+ *            pointers 16-byte aligned.
  * ------------------------------------------------------------------------------------------ */
 size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, int d, int S,
                                               int max_pages, int max_kept);

@@ -274,7 +274,12 @@ def test_attn_invalid_device_data_gives_nan_rows():
         if r in (1, 3):
             assert torch.isnan(out[rows].float()).all() and torch.isnan(lse[rows]).all()
         else:
-            assert torch.equal(out[rows], ref[rows]) and torch.equal(lse[rows], ref_lse[rows])
+            # the other requests keep their results; not bit for bit, since a request's key
+            # range may be cut at other places once the columns of requests 1 and 3 change
+            assert torch.isfinite(out[rows].float()).all()
+            oerr = (out[rows].float() - ref[rows].float()).abs().max().item()
+            lerr = (lse[rows] - ref_lse[rows]).abs().max().item()
+            assert oerr <= OUT_TOL and lerr <= LSE_TOL, (r, oerr, lerr)
 
 
 def test_step_edge_cases_empty_prefix_and_nothing_masked():
@@ -327,3 +332,34 @@ def test_attn_output_rounds_to_nearest_even():
     got = out.float().cpu().numpy()
     assert np.all(got == 1.0 + 1.0 / 64), np.unique(got)
     assert np.allclose(lse.cpu().numpy(), np.log(64.0), atol=1e-6)
+
+
+def test_attn_shared_workspace_across_calls():
+    # one zero-filled workspace serves a sequence of calls of different shapes, each with many
+    # cut items (few requests, long prefixes): the arrival counters must come back to zero after
+    # every call, or a later call would merge the wrong pieces
+    _announce("attn shared workspace")
+    seq = ["g8_d128_s16_split", "g4_d128_s64", "g4_long_split", "g8_d128_s16_split"]
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    for case in seq:
+        name, over, max_kept = ATTN_CASES[case]
+        over = dict(over)
+        over.setdefault("budget", ("fixed", max_kept))
+        over["score_dtype"] = "bf16"
+        st = make_step(BY_NAME[name].scaled(**over))
+        keep = _random_keep(np.random.default_rng(11), st.B, st.blk, max_kept, empty_frac=0.0)
+        c = attn_case_inputs(st, keep)
+        ref_out, ref_lse = oracle_attention(st, c["q_rows64"], c["offsets"])
+        t = step_inputs(st)
+        need = F.attn_workspace_bytes(st.B, st.blk, st.Hq, st.Hkv, st.d, st.S,
+                                      st.page_table.shape[1], max_kept)
+        assert need <= ws.numel()
+        for _ in range(2):
+            out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache,
+                                           t.page_table, t.prefix_len, t.k_blk, t.v_blk,
+                                           max_kept, st.sm_scale, workspace=ws)
+            torch.cuda.synchronize()
+            T = int(c["offsets"][-1])
+            oerr = np.abs(out[:T].float().cpu().numpy() - ref_out).max()
+            lerr = np.abs(lse[:T].cpu().numpy() - ref_lse).max()
+            assert oerr <= OUT_TOL and lerr <= LSE_TOL, (case, oerr, lerr)
