@@ -72,8 +72,9 @@ def counter_traffic(workload):
 
 
 def cpu_baseline(recipe, budget_s):
-    """The fp64 oracle timed on a bounded sample of the same workload (fewer requests drawn from
-    the same distributions), scaled to focused tokens per second."""
+    """The fp64 oracle timed on a bounded sample of the same workload (batches of 16 requests
+    drawn from the same distributions, new seeds each batch, until about budget_s seconds of
+    oracle time), scaled to focused tokens per second."""
     import oracle
     from workloads import make_step
     try:
@@ -84,7 +85,7 @@ def cpu_baseline(recipe, budget_s):
     Bs = 16
     total_t, total_tok, reqs = 0.0, 0, 0
     seed = recipe.seed
-    while total_t < budget_s and reqs < recipe.B:
+    while total_t < budget_s:
         st = make_step(recipe.scaled(B=Bs), seed=seed)
         t0 = time.perf_counter()
         res = oracle.step(st)
@@ -94,9 +95,107 @@ def cpu_baseline(recipe, budget_s):
         seed += 1
     return {"value": total_tok / total_t, "unit": "focused tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{reqs} requests of {recipe.name} in batches of {Bs} (seeds from "
-                      f"{recipe.seed}), full step score+select+compact+attend in fp64, "
-                      f"{total_t:.1f} s wall"}
+            "sample": f"{reqs} requests of {recipe.name} in batches of {Bs} (seeds {recipe.seed}.."
+                      f"{seed - 1}), full step score+select+compact+attend in fp64, "
+                      f"{total_t:.1f} s of oracle time"}
+
+
+# ------------------------------------------------------------------------------------------
+# profile summaries (run on the CSV output of the rocprofv3 commands listed in PROFILE_CMDS)
+# ------------------------------------------------------------------------------------------
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o trace "
+             "-- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+    "step_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/step_fetch "
+                  "-o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "step_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/step_write "
+                  "-o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/copy_fetch "
+                  "-o run -- python3 bench.py --calibrate",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/copy_write "
+                  "-o run -- python3 bench.py --calibrate",
+}
+
+
+def _find(root, pattern):
+    import glob
+    hits = sorted(glob.glob(os.path.join(root, "**", pattern), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"{pattern} under {root}")
+    return hits[0]
+
+
+def _short(name):
+    import re
+    m = re.search(r"::(\w+)(<[^(]*>)?\(", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    m = re.search(r"\w+", name)
+    return m.group(0) if m else name[:60]
+
+
+def _counter_per_dispatch(root, counter):
+    """{kernel short name: [value per dispatch]} from a rocprofv3 --pmc CSV."""
+    import csv
+    vals = {}
+    with open(_find(root, "*counter_collection.csv")) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(_short(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def summarize_profiles(out_root, workload):
+    """Writes profiles/kernels_<workload>.txt (kernel-trace statistics) and
+    profiles/attn_traffic_<workload>.{json,txt} (HBM bytes per attention launch from FETCH_SIZE /
+    WRITE_SIZE, each scaled by what the counter reads for a 1 GiB device copy)."""
+    import csv
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    rows = list(csv.DictReader(open(_find(os.path.join(out_root, "prof"), "*kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"# command: {PROFILE_CMDS['trace']}",
+             f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name'])[:72]:72s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
+    with open(os.path.join(prof, f"kernels_{workload}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    pmc = os.path.join(out_root, "pmc")
+    med = lambda v: sorted(v)[len(v) // 2]
+    gib = float(1 << 30)
+    cf = _counter_per_dispatch(os.path.join(pmc, "copy_fetch"), "FETCH_SIZE")
+    cw = _counter_per_dispatch(os.path.join(pmc, "copy_write"), "WRITE_SIZE")
+    # the calibration copy is the one dispatch whose byte counts are near 1 GiB
+    copy_f = max(max(v) for v in cf.values()) * 1024.0
+    copy_w = max(max(v) for v in cw.values()) * 1024.0
+    f_fac, w_fac = gib / copy_f, gib / copy_w
+    sf = _counter_per_dispatch(os.path.join(pmc, "step_fetch"), "FETCH_SIZE")
+    sw = _counter_per_dispatch(os.path.join(pmc, "step_write"), "WRITE_SIZE")
+    key = next(k for k in sf if k.startswith("attn_kernel"))
+    fetch = med(sf[key]) * 1024.0 * f_fac
+    write = med(sw[key]) * 1024.0 * w_fac
+    rec = {"workload": workload, "kernel": key, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": med(sf[key]), "write_kib_per_dispatch": med(sw[key]),
+           "fetch_scale": f_fac, "write_scale": w_fac,
+           "hbm_bytes_per_launch": int(round(fetch + write)),
+           "hbm_read_bytes": int(round(fetch)), "hbm_write_bytes": int(round(write)),
+           "commands": [PROFILE_CMDS[k] for k in ("step_fetch", "step_write", "copy_fetch",
+                                                  "copy_write")]}
+    with open(os.path.join(prof, f"attn_traffic_{workload}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    txt = [f"# HBM traffic of {key}, workload {workload}",
+           *[f"# command: {c}" for c in rec["commands"]],
+           f"copy calibration: 1 GiB copy reads as FETCH_SIZE {copy_f / 1024:.0f} KiB "
+           f"(scale {f_fac:.3f}), WRITE_SIZE {copy_w / 1024:.0f} KiB (scale {w_fac:.3f})",
+           f"attention per launch: FETCH_SIZE {med(sf[key]):.0f} KiB -> {fetch / 1e6:.1f} MB read; "
+           f"WRITE_SIZE {med(sw[key]):.0f} KiB -> {write / 1e6:.1f} MB written; "
+           f"total {(fetch + write) / 1e6:.1f} MB"]
+    with open(os.path.join(prof, f"attn_traffic_{workload}.txt"), "w") as fh:
+        fh.write("\n".join(txt) + "\n")
+    print("\n".join(lines + txt))
 
 
 def main():
@@ -107,6 +206,9 @@ def main():
     ap.add_argument("--workload", default="sdar_b256_blk32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--summarize-profiles", metavar="OUT_ROOT",
+                    help="write the profiles/ summaries from the CSV output of the rocprofv3 "
+                         "commands in PROFILE_CMDS (run with OUT_ROOT as their gpurun_out)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes) 5 times, "
                          "to scale HBM byte counters")
@@ -116,6 +218,9 @@ def main():
               "for how the step would shard by request).", file=sys.stderr)
         sys.exit(2)
 
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
     import torch
     if args.calibrate:
         n = 1 << 30
