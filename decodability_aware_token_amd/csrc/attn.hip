@@ -10,8 +10,8 @@
 // streamed as 32-key tiles (columns), the prefix tiles first, then the block tiles.  The columns
 // of all requests form one global list.
 //
-// Column groups.  The grid holds as many waves as the GPU runs at once, in groups of Hkv*nqg
-// waves, one wave per (kv head, query group).  Group i takes the i-th of equal contiguous slices
+// Column groups.  The grid is persistent, one 4-wave workgroup per CU, its waves in groups of
+// Hkv*nqg, one wave per (kv head, query group).  Group i takes the i-th of equal contiguous slices
 // of the column list, so the waves of a group stream the same pages of the same requests at the
 // same time, each its own kv head's part of the page: every page is read by all its heads
 // together, which keeps the DRAM accesses local wherever the slices fall.  A wave streams its
@@ -42,6 +42,12 @@ namespace focus {
 namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup
+// Tile buffers per wave (NB - 1 tiles in flight during a compute) and workgroups per CU for one
+// query tile per item.  Measured on MI355X: one wave per SIMD with one tile in flight streams
+// faster than two waves per SIMD or deeper prefetch; fewer concurrent streams keep the DRAM
+// accesses more local, and the CU's outstanding misses are the limit, not the wave count.
+constexpr int kPrefetchQt1 = 2;
+constexpr int kWgsPerCuQt1 = 1;
 // s_waitcnt immediate with vmcnt = 0 and the other counters at their maxima (GFX9 encoding):
 // waits until every vector memory access of the wave, stores included, has completed
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -183,10 +189,10 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      T.k[s][kk] = load16v(kp + ((size_t)(((4 * kk) << log2S) + 4 * s) << 3));
+      T.k[s][kk] = load16_stream(kp + ((size_t)(((4 * kk) << log2S) + 4 * s) << 3));
   const uint16_t* vp = vbase + ((size_t)((vg & (S - 1)) >> 3) * D + m16) * 8;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) T.v[dt] = load16v(vp + 16 * dt * 8);
+  for (int dt = 0; dt < ND; ++dt) T.v[dt] = load16_stream(vp + 16 * dt * 8);
 }
 
 // Loads the B operand (Q^T) of the cursor's item.  Rows past the item's rows (or past cap) are
@@ -280,8 +286,8 @@ __device__ __forceinline__ int slice_begin(int i, int total, int n) {
 }
 
 // page_table is a separate restrict argument so that its (uniform) reads become scalar loads.
-template <int D, int QT>
-__global__ __launch_bounds__(256, (QT >= 2 ? 1 : 2)) void attn_kernel(
+template <int D, int QT, int NB>
+__global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel(
     Params p, const int32_t* __restrict__ page_table) {
   constexpr int NK = D / 32, ND = D / 16, R = 16 * QT;
   extern __shared__ __align__(16) int smem_i[];
@@ -544,30 +550,35 @@ __global__ __launch_bounds__(256, (QT >= 2 ? 1 : 2)) void attn_kernel(
     }
     if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  // ---- stream: compute tile tv (cursor C, buffer X) while tile tv+1 (cursor L, buffer Y) is
-  // in flight; tv counts tiles in processing order.  Past the slice end L stays on the last
-  // tile, so the prefetch is unconditional (it re-reads that tile: cache hits).  When C starts a
-  // piece its queries are loaded before Y's tile, so the compute's wait does not drain Y.
+  // ---- stream: compute tile tv (cursor C) from buffer tv % NB while the next NB-1 tiles
+  // (up to cursor L) are in flight; tv counts tiles in processing order.  Past the slice end L
+  // stays on the last tile, so the prefetch is unconditional (it re-reads that tile: cache
+  // hits).  When C starts a piece its queries are loaded before the next prefetch, so the
+  // compute's wait does not drain the tiles in flight.
   u32x4_t qf[QT][NK];
   load_q<D, QT>(qf, C, p, lane);
   Cursor L = C;
-  int tvl = 0;  // processing index of L
-  auto step_l = [&]() {
-    if (tvl + 1 == n1)
-      L = Ca;
+  int tvl = 0, tvc = 0;  // processing indices of L and C
+  auto next = [&](Cursor& c, int& idx) {
+    if (idx + 1 == n1)
+      c = Ca;
     else
-      advance(L, meta, p);
-    ++tvl;
+      advance(c, meta, p);
+    ++idx;
   };
-  if (n > 1) step_l();
   bool bad = false;
-  Tile<D> ta, tb;
-  load_tile<D>(ta, C, fetch_pages(C, p, page_table), p, lane);
+  Tile<D> tl[NB];
+#pragma unroll
+  for (int k = 0; k < NB - 1; ++k) {
+    if (k > 0 && tvl + 1 < n) next(L, tvl);
+    load_tile<D>(tl[k], L, fetch_pages(L, p, page_table), p, lane);
+  }
+  if (tvl + 1 < n) next(L, tvl);
   int tv = 0;
 
   // A step past the slice end only issues its (cache-hitting) prefetch, so that the loop has a
-  // single exit, after every second step: an exit between the two buffer roles would let the
-  // compiler merge the two roles' pending loads at the loop head and drain the prefetch there.
+  // single exit, after every NB steps: an exit between two buffer roles would let the compiler
+  // merge the roles' pending loads at the loop head and drain the prefetch there.
   auto step = [&](Tile<D>& X, Tile<D>& Y) {
     const bool live = tv < n;
     if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
@@ -585,13 +596,13 @@ __global__ __launch_bounds__(256, (QT >= 2 ? 1 : 2)) void attn_kernel(
         bad = false;
       }
     }
-    C = L;
-    if (tvl + 1 < n) step_l();
+    if (tvc + 1 < n) next(C, tvc);
+    if (tvl + 1 < n) next(L, tvl);
     ++tv;
   };
   while (true) {
-    step(ta, tb);
-    step(tb, ta);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) step(tl[j], tl[(j + NB - 1) % NB]);
     if (tv >= n) break;
   }
 }
@@ -619,7 +630,8 @@ int device_cus() {
 template <int D, int QT>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
   const size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
-  hipLaunchKernelGGL((attn_kernel<D, QT>), dim3(plan.wgs), dim3(256), shmem, s, prm,
+  constexpr int NB = QT == 1 ? kPrefetchQt1 : 2;
+  hipLaunchKernelGGL((attn_kernel<D, QT, NB>), dim3(plan.wgs), dim3(256), shmem, s, prm,
                      prm.page_table);
   return hipGetLastError();
 }
@@ -632,9 +644,9 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
   const int rows = max_kept * G;
   pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
-  // as many 4-wave workgroups as the GPU holds at once: 2 waves per SIMD with one query tile
-  // (registers <= 256), else 1 wave per SIMD
-  pl.wgs = device_cus() * (pl.qt == 1 ? 2 : 1);
+  // one 4-wave workgroup per CU (one wave per SIMD, each with NB tiles of 32 keys in flight)
+  pl.wgs = device_cus() * kWgsPerCuQt1;
+  if (pl.qt > 1) pl.wgs = device_cus();
   const long long ntiles_max = ((long long)max_pages * S + 31) / 32 + (blk + 31) / 32;
   pl.tiles_bound = (long long)B * ntiles_max;
   pl.gs = Hkv * pl.nqg;

@@ -53,4 +53,9 @@ __device__ __forceinline__ u32x4_t load16v(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// 16-byte load of data read exactly once (non-temporal: the caches do not keep it)
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 }  // namespace focus
