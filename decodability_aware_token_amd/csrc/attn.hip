@@ -28,11 +28,11 @@
 //
 // Register operands straight from HBM (no LDS):
 //   * K pages [page, Hkv, d/8, S, 8]: a lane's 16-byte load is 8 dims of one key; the tile is the
-//     A operand of S^T = K Q^T; key slot m of subtile s is key 8*(m/4) + 4*s + m%4, chosen so
-//     that the result lane group j holds exactly keys 8j..8j+7 of the tile.
-//   * V pages [page, Hkv, S/8, d, 8]: a lane's 16-byte load is one dim of 8 consecutive keys,
-//     which is exactly the A operand of O^T = V^T P^T for lane group j (256 contiguous bytes per
-//     quarter-wave); P^T (bf16) comes straight from the S^T registers.
+//     A operand of S^T = K Q^T, key slot m of subtile s being key 16s + m (whole 256-byte runs
+//     per load instruction).
+//   * V pages [page, Hkv, S/8, d, 8]: a lane's two 8-byte loads are one dim of the two 4-key
+//     runs its S^T lane group holds, which is exactly the A operand of O^T = V^T P^T for that
+//     lane group; P^T (bf16) comes straight from the S^T registers.
 // Softmax is online in the exp2 domain (f32).  Merges run in a fixed order, so results are
 // bitwise reproducible.
 #include "device_common.h"
@@ -148,9 +148,14 @@ __device__ __forceinline__ Pages fetch_pages(const Cursor& c, const Params& p,
   return pg;
 }
 
-// Loads the cursor's tile.  Branch-free: each lane's 8-key group is clamped to the group of the
-// segment's last valid key, which lies in an allocated page; keys past the valid length are
-// masked in compute_tile.  An out-of-range page id is replaced by page 0 and reported in T.bad.
+// Loads the cursor's tile.  Key slot m of K subtile s is key 16s + m, so each K load
+// instruction reads 16 consecutive keys of one 8-dim group: whole 256-byte runs.  The S^T
+// result lane group j then holds keys 4j..4j+3 (subtile 0) and 16+4j..16+4j+3 (subtile 1), and
+// the V operand of that lane group is loaded as the same two 4-key runs (8 bytes each; a load
+// instruction again covers whole 256-byte runs).  Branch-free: keys are clamped to the last
+// valid key (runs to the last valid run), which lie in allocated pages; keys past the valid
+// length are masked in compute_tile.  An out-of-range page id is replaced by page 0 and
+// reported in T.bad.
 template <int D>
 __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg, const Params& p,
                                           int lane) {
@@ -163,36 +168,46 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
   const int log2S = paged ? p.log2S : p.log2blk;
   const int S = 1 << log2S;
   const size_t page_elems = (size_t)D << log2S;  // one (page, kv head) block
-  const int last_group = (nvalid - 1) & ~7;
-  const int kg = min(key0 + 8 * (m16 >> 2), last_group);
-  const int vg = min(key0 + 8 * j4, last_group);
-  const uint16_t* kbase;
-  const uint16_t* vbase;
-  if (paged) {
-    const int p0 = key0 >> log2S;
-    int pk = ((kg >> log2S) == p0) ? pg.a : pg.b;
-    int pv = ((vg >> log2S) == p0) ? pg.a : pg.b;
-    const bool okk = pk >= 0 && pk < p.num_pages, okv = pv >= 0 && pv < p.num_pages;
-    T.bad = !okk || !okv;
-    pk = okk ? pk : 0;
-    pv = okv ? pv : 0;
-    kbase = p.k_cache + ((size_t)pk * p.Hkv + c.g) * page_elems;
-    vbase = p.v_cache + ((size_t)pv * p.Hkv + c.g) * page_elems;
-  } else {
-    T.bad = false;
-    kbase = p.k_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
-    vbase = p.v_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
-  }
-  const int kslot = (kg & (S - 1)) + (m16 & 3);
-  const uint16_t* kp = kbase + ((size_t)((j4 << log2S) + kslot) << 3);
+  const int last = nvalid - 1, last_run = last & ~3;
+  const uint16_t* kb[2];
+  const uint16_t* vb[2];
+  int kkey[2], vrun[2];
+  bool bad = false;
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < 2; ++s) {
+    kkey[s] = min(key0 + 16 * s + m16, last);
+    vrun[s] = min(key0 + 16 * s + 4 * j4, last_run);
+    if (paged) {
+      const int p0 = key0 >> log2S;
+      int pk = ((kkey[s] >> log2S) == p0) ? pg.a : pg.b;
+      int pv = ((vrun[s] >> log2S) == p0) ? pg.a : pg.b;
+      const bool okk = pk >= 0 && pk < p.num_pages, okv = pv >= 0 && pv < p.num_pages;
+      bad = bad || !okk || !okv;
+      pk = okk ? pk : 0;
+      pv = okv ? pv : 0;
+      kb[s] = p.k_cache + ((size_t)pk * p.Hkv + c.g) * page_elems;
+      vb[s] = p.v_cache + ((size_t)pv * p.Hkv + c.g) * page_elems;
+    } else {
+      kb[s] = p.k_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
+      vb[s] = p.v_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
+    }
+  }
+  T.bad = bad;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint16_t* kp = kb[s] + ((size_t)((j4 << log2S) + (kkey[s] & (S - 1))) << 3);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      T.k[s][kk] = load16_stream(kp + ((size_t)(((4 * kk) << log2S) + 4 * s) << 3));
-  const uint16_t* vp = vbase + ((size_t)((vg & (S - 1)) >> 3) * D + m16) * 8;
+      T.k[s][kk] = load16_stream(kp + ((size_t)((4 * kk) << log2S) << 3));
+  }
+  const uint16_t* vp0 = vb[0] + ((size_t)((vrun[0] & (S - 1)) >> 3) * D + m16) * 8 + (vrun[0] & 4);
+  const uint16_t* vp1 = vb[1] + ((size_t)((vrun[1] & (S - 1)) >> 3) * D + m16) * 8 + (vrun[1] & 4);
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) T.v[dt] = load16_stream(vp + 16 * dt * 8);
+  for (int dt = 0; dt < ND; ++dt) {
+    const u32x2_t lo = load8_stream(vp0 + 16 * dt * 8);
+    const u32x2_t hi = load8_stream(vp1 + 16 * dt * 8);
+    T.v[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
 }
 
 // Loads the B operand (Q^T) of the cursor's item.  Rows past the item's rows (or past cap) are
@@ -220,14 +235,17 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
                                              float (&lrun)[QT], float scale_log2, int lane) {
   constexpr int NK = D / 32, ND = D / 16;
   const int j4 = lane >> 4;
-  const int kbase = key0 + 8 * j4;  // this lane group's 8 keys: kbase + 0..7
+  // this lane group's 8 keys: slots 0..3 are keys key0 + 4j + (0..3), slots 4..7 are keys
+  // key0 + 16 + 4j + (0..3); nv[r] = valid keys of run r
+  const int nv[2] = {nvalid - (key0 + 4 * j4), nvalid - (key0 + 16 + 4 * j4)};
   // Values of keys past the end are zeroed: their weights are zero, but the loaded values may
   // be anything and 0 * NaN would not vanish.  Branch-free (all-ones masks on full tiles).
-  const int nv = nvalid - kbase;
   u32x4_t vmask;
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
-    vmask[w] = (2 * w + 1 < nv) ? 0xffffffffu : ((2 * w < nv) ? 0x0000ffffu : 0u);
+  for (int w = 0; w < 4; ++w) {
+    const int n = nv[w >> 1], b = 2 * (w & 1);
+    vmask[w] = (b + 1 < n) ? 0xffffffffu : ((b < n) ? 0x0000ffffu : 0u);
+  }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -243,7 +261,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
       x[4 + i] = s1[i] * scale_log2;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (e < nv) ? x[e] : -INFINITY;
+    for (int e = 0; e < 8; ++e) x[e] = ((e & 3) < nv[e >> 2]) ? x[e] : -INFINITY;
     float mx = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);

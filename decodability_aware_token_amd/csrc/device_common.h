@@ -53,6 +53,13 @@ __device__ __forceinline__ u32x4_t load16v(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 8-byte load of data read exactly once (non-temporal: the caches do not keep it)
+__device__ __forceinline__ u32x2_t load8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
 // 16-byte load of data read exactly once (non-temporal: the caches do not keep it)
 __device__ __forceinline__ u32x4_t load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
