@@ -5,7 +5,7 @@ layer 0), budgeted top-k selection, compaction + gather of the hidden states and
 attention queries, and ragged paged attention over each request's paged prefix plus block KV.
 Inputs are seeded synthetic tensors already resident in HBM.  One JSON line is printed.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-graph]
 """
 from __future__ import annotations
 
@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdar_b256_blk32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager launches instead of HIP graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--summarize-profiles", metavar="OUT_ROOT",
                     help="write the profiles/ summaries from the CSV output of the rocprofv3 "
@@ -257,10 +259,12 @@ def main():
         fs.run()
     torch.cuda.synchronize()
 
+    # Pass 1 (eager, per-stage HIP events on the launch stream): the stage breakdown and the
+    # attention kernel's launch duration for the roofline.
     stages = ("score", "select", "compact_hidden", "compact_q", "attend")
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] eager pass: {args.steps} steps with per-stage events")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -269,7 +273,7 @@ def main():
             getattr(fs, name)()
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    eager_wall = time.perf_counter() - t0
     per_stage = np.zeros(len(stages))
     step_ms = np.zeros(args.steps)
     for i in range(args.steps):
@@ -277,7 +281,24 @@ def main():
             per_stage[j] += ev[i][j].elapsed_time(ev[i][j + 1])
         step_ms[i] = ev[i][0].elapsed_time(ev[i][-1])
     per_stage /= args.steps
-    ms_per_step = wall * 1000.0 / args.steps
+    eager_ms = eager_wall * 1000.0 / args.steps
+
+    # Pass 2 (the measured step): the whole step captured once in a HIP graph, W untimed
+    # replays, then exactly K replays between device synchronisations.
+    ms_per_step = eager_ms
+    mode = "eager"
+    if not args.no_graph:
+        fs.capture()
+        for _ in range(args.warmup):
+            fs.replay()
+        log(f"[bench] graph pass: {args.steps} replays")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fs.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1000.0 / args.steps
+        mode = "hip graph"
 
     offsets = fs.offsets.cpu().numpy()
     kept = np.diff(offsets)
@@ -288,8 +309,9 @@ def main():
     sb, sf = score_algorithmic(st)
     for j, name in enumerate(stages):
         log(f"[bench] {name:15s} {per_stage[j] * 1000:9.1f} us")
-    log(f"[bench] step (events) {step_ms.mean() * 1000:.1f} us median {np.median(step_ms) * 1000:.1f}"
-        f" us; wall {ms_per_step * 1000:.1f} us; T={T}")
+    log(f"[bench] eager step (events) {step_ms.mean() * 1000:.1f} us median "
+        f"{np.median(step_ms) * 1000:.1f} us; eager wall {eager_ms * 1000:.1f} us; "
+        f"{mode} wall {ms_per_step * 1000:.1f} us; T={T}")
     log(f"[bench] attention {attn_bytes / 1e6:.1f} MB algorithmic -> {achieved:.0f} GB/s "
         f"({achieved / PEAK_HBM_GBS * 100:.1f}% of HBM), "
         f"{attn_flops / (attn_ms * 1e-3) / 1e12:.2f} TFLOP/s")
@@ -317,6 +339,7 @@ def main():
             "hidden": recipe.hidden, "kept_tokens": T, "block_tokens": st.B * st.blk,
             "block_tokens_per_s": st.B * st.blk / (ms_per_step * 1e-3),
             "stage_us": {n: round(per_stage[j] * 1000, 2) for j, n in enumerate(stages)},
+            "step_launch": mode, "eager_ms_per_step": round(eager_ms, 5),
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kMaxB = 4096;
+constexpr int64_t kMaxRowBytes = int64_t(1) << 24;  // 16 MiB per gathered row
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -75,7 +76,9 @@ int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* 
   a.d = d;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.delta = delta;
-  a.part = static_cast<float*>(workspace);
+  a.counters = static_cast<int*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                    focus::score_counter_bytes(B));
   return status_of(focus::launch_score(a, stream));
 }
 
@@ -112,7 +115,8 @@ int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t
   if (!pow2_in(blk, 16, 64) || B > kMaxB) return FOCUS_ERR_UNSUPPORTED;
   if (rows) {
     if (row_bytes <= 0) return FOCUS_ERR_INVALID_ARG;
-    if (row_bytes % 16 != 0 || !aligned16(rows) || !aligned16(gathered))
+    if (row_bytes % 16 != 0 || row_bytes > kMaxRowBytes || !aligned16(rows) ||
+        !aligned16(gathered))
       return FOCUS_ERR_UNSUPPORTED;
   }
   focus::CompactArgs a{};

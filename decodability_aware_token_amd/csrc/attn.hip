@@ -48,9 +48,6 @@ constexpr int kWaves = 4;  // waves per workgroup
 // accesses more local, and the CU's outstanding misses are the limit, not the wave count.
 constexpr int kPrefetchQt1 = 2;
 constexpr int kWgsPerCuQt1 = 1;
-// s_waitcnt immediate with vmcnt = 0 and the other counters at their maxima (GFX9 encoding):
-// waits until every vector memory access of the wave, stores included, has completed
-constexpr int kWaitVmcnt0 = 0x0F70;
 // cache-policy bits of a vector memory access with device scope (SC1): stores write through to
 // the device-coherent level, loads read from it (what device-scope atomics use on gfx950)
 constexpr int kCpolDevice = 16;

@@ -2,15 +2,18 @@
 // FOCUS, section "Arquitetura do FOCUS" (compact the state, drop evicted tokens); project page
 // "FOCUS: DLLMs Know How to Tame Their Compute Bound", card "Runtime Action" (ragged execution).
 //
-// One workgroup per request r, 256 threads.
-//  1. base = offsets[r] = number of kept tokens of requests 0..r-1: every thread counts the
-//     nonzero bytes of a strided subset of the predecessors' keep rows (4 bytes at a time), then a
-//     fixed-order LDS tree sums the 256 partial counts.  Integer arithmetic: exact and
-//     deterministic.  (Quadratic in B in total, which is cheap for the supported B <= 4096 since
-//     the keep rows are read from L2.)
-//  2. Wave 0: lane j tests keep[r, j]; a ballot gives k_r and the lane's rank among the kept
-//     lanes (mbcnt), so kept_pos[base + rank] = j lists positions in ascending order.
-//  3. All threads copy the k_r rows with 16-byte loads, several chunks in flight per thread.
+// One workgroup per request r, 256 threads, ordered so that the memory round trips overlap:
+//  1. Every thread issues its loads of the predecessors' keep rows (4 bytes at a time, a first
+//     batch of up to 16 words per thread in flight at once).
+//  2. Wave 0: lane j tests keep[r, j]; a ballot gives k_r and each kept lane's rank (mbcnt), so
+//     the kept positions come out in ascending order.
+//  3. All threads issue the loads of the first batch of the k_r rows to gather (16 bytes each);
+//     they do not depend on where the rows go.
+//  4. base = offsets[r] = kept tokens of requests 0..r-1: the nonzero bytes of the predecessors'
+//     keep rows, summed per wave by a fixed xor butterfly and over the 4 waves in order.
+//     Integer arithmetic: exact and deterministic.  (Quadratic in B in total, which is cheap
+//     for the supported B <= 4096 since the keep rows are read from L2.)
+//  5. kept_pos[base + rank] = j, offsets[r + 1] = base + k_r, and the gathered rows are stored.
 #include "device_common.h"
 #include "launch.h"
 
@@ -24,77 +27,112 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
   return __popc(w & 0x01010101u);
 }
 
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+constexpr int kCountBatch = 16;  // predecessor keep words per thread in the first batch
+constexpr int kGatherBatch = 8;  // 16-byte chunks per thread per gather batch
+
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
-  __shared__ int s_cnt[256];
+  __shared__ int s_wsum[4];
   __shared__ int s_pos[64];
-  __shared__ int s_base, s_k;
-  const int tid = threadIdx.x;
+  __shared__ int s_k;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = blockIdx.x;
   const int blk = a.blk;
   const int words = blk / 4;  // keep row as 32-bit words (rows are 16/32/64 bytes)
 
-  // 1. kept tokens of the predecessors
-  int cnt = 0;
+  // Loads are branch-free (clamped addresses, results masked afterwards), so that the compiler
+  // can wait for each group of loads alone instead of for everything in flight.
+  // this request's keep byte (every wave: the ballot below needs no branch), loaded first so
+  // that the ballot waits for it alone
+  const uint8_t kb = a.keep[(size_t)r * blk + min(lane, blk - 1)];
+
+  // 1. first batch of predecessor keep words
   const uint32_t* kw = reinterpret_cast<const uint32_t*>(a.keep);
   const int nw = r * words;
-  for (int w = tid; w < nw; w += 256) cnt += nonzero_bytes(kw[w]);
-  s_cnt[tid] = cnt;
-  __syncthreads();
-  for (int stride = 128; stride > 0; stride >>= 1) {
-    if (tid < stride) s_cnt[tid] += s_cnt[tid + stride];
-    __syncthreads();
+  uint32_t cw[kCountBatch];
+#pragma unroll
+  for (int u = 0; u < kCountBatch; ++u) {
+    const int w = tid + 256 * u;
+    cw[u] = kw[min(w, max(nw - 1, 0))];
   }
+  __builtin_amdgcn_sched_barrier(0);  // issue all of them before the ballot waits
+#pragma unroll
+  for (int u = 0; u < kCountBatch; ++u)
+    if (tid + 256 * u >= nw) cw[u] = 0u;
 
-  // 2. this request's kept positions
-  if (tid < 64) {
-    const bool kj = tid < blk && a.keep[(size_t)r * blk + tid] != 0;
-    const uint64_t bits = __ballot(kj);
-    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
-    const int base = s_cnt[0];
-    const int k = __popcll(bits);
-    if (kj) {
-      s_pos[rank] = tid;
-      if (a.kept_pos != nullptr && base + rank < a.cap) a.kept_pos[base + rank] = tid;
-    }
-    if (tid == 0) {
-      s_base = base;
-      s_k = k;
-      a.offsets[r + 1] = base + k;
+  // 2. this request's kept positions (every wave computes the ballot; wave 0 publishes it)
+  const bool kj = lane < blk && kb != 0;
+  const uint64_t bits = __ballot(kj);
+  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+  if (wv == 0) {
+    if (kj) s_pos[rank] = lane;
+    if (lane == 0) s_k = __popcll(bits);
+  }
+  __syncthreads();
+  const int k_all = s_k;
+
+  // 3. first gather batch: loads only
+  const bool gather = a.gathered != nullptr && k_all > 0;
+  const int chunks = gather ? (int)(a.row_bytes / 16) : 0;  // row_bytes <= 2^24
+  const int total = k_all * chunks;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rows);
+  unsigned char* dst = reinterpret_cast<unsigned char*>(a.gathered);
+  auto src_of = [&](int c) {
+    const int t = c / chunks, cc = c - t * chunks;
+    return src + ((int64_t)r * blk + s_pos[t]) * a.row_bytes + (int64_t)cc * 16;
+  };
+  // unconditional (a request with nothing to gather reads 16 bytes of its own keep row), so
+  // that no join makes the compiler wait for these loads before the count below
+  const unsigned char* dummy = a.keep + (size_t)r * blk;
+  uint4 v[kGatherBatch];
+#pragma unroll
+  for (int u = 0; u < kGatherBatch; ++u)
+    v[u] = load16(total > 0 ? src_of(min(tid + u * 256, total - 1)) : dummy);
+
+  // 4. base = kept tokens of the predecessors
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < kCountBatch; ++u) cnt += nonzero_bytes(cw[u]);
+  for (int w = tid + 256 * kCountBatch; w < nw; w += 256) cnt += nonzero_bytes(kw[w]);
+  cnt = wave_sum_int(cnt);
+  if (lane == 0) s_wsum[wv] = cnt;
+  __syncthreads();
+  const int base = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+
+  // 5. outputs
+  if (wv == 0) {
+    if (kj && a.kept_pos != nullptr && base + rank < a.cap) a.kept_pos[base + rank] = lane;
+    if (lane == 0) {
+      a.offsets[r + 1] = base + k_all;
       if (r == 0) a.offsets[0] = 0;
     }
   }
-  __syncthreads();
-
-  // 3. gather
-  if (a.gathered == nullptr) return;
-  const int base = s_base;
-  const int k = min(s_k, a.cap - base);
+  if (!gather) return;
+  const int k = min(k_all, a.cap - base);  // rows at or past cap are not written
   if (k <= 0) return;
-  const int64_t chunks = a.row_bytes / 16;
-  const int64_t total = (int64_t)k * chunks;
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rows);
-  unsigned char* dst = reinterpret_cast<unsigned char*>(a.gathered);
-  constexpr int U = 4;
-  for (int64_t c0 = tid; c0 < total; c0 += 256 * U) {
-    uint4 v[U];
+  const int limit = k * chunks;
+  auto dst_of = [&](int c) {
+    const int t = c / chunks, cc = c - t * chunks;
+    return dst + ((int64_t)base + t) * a.row_bytes + (int64_t)cc * 16;
+  };
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + (int64_t)u * 256;
-      if (c < total) {
-        const int t = (int)(c / chunks);
-        const int64_t cc = c - (int64_t)t * chunks;
-        v[u] = load16(src + ((int64_t)r * blk + s_pos[t]) * a.row_bytes + cc * 16);
-      }
-    }
+  for (int u = 0; u < kGatherBatch; ++u) {
+    const int c = tid + u * 256;
+    if (c < limit) *reinterpret_cast<uint4*>(dst_of(c)) = v[u];
+  }
+  for (int c0 = tid + 256 * kGatherBatch; c0 < limit; c0 += 256 * kGatherBatch) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + (int64_t)u * 256;
-      if (c < total) {
-        const int t = (int)(c / chunks);
-        const int64_t cc = c - (int64_t)t * chunks;
-        *reinterpret_cast<uint4*>(dst + ((int64_t)base + t) * a.row_bytes + cc * 16) = v[u];
-      }
+    for (int u = 0; u < kGatherBatch; ++u) v[u] = load16(src_of(min(c0 + u * 256, limit - 1)));
+#pragma unroll
+    for (int u = 0; u < kGatherBatch; ++u) {
+      const int c = c0 + u * 256;
+      if (c < limit) *reinterpret_cast<uint4*>(dst_of(c)) = v[u];
     }
   }
 }

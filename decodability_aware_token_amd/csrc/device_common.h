@@ -55,6 +55,10 @@ __device__ __forceinline__ u32x4_t load16v(const void* p) {
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// s_waitcnt immediate with vmcnt = 0 and the other counters at their maxima (GFX9 encoding):
+// waits until every vector memory access of the wave, stores included, has completed
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // 8-byte load of data read exactly once (non-temporal: the caches do not keep it)
 __device__ __forceinline__ u32x2_t load8_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));

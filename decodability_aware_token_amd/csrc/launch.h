@@ -17,8 +17,10 @@ struct ScoreArgs {
   int B, blk, Hq, Hkv, d;
   float scale_log2;  // sm_scale * log2(e)
   float* delta;      // [B, blk]
+  int* counters;     // workspace [B] arrival counters (zero between calls)
   float* part;       // workspace [B, Hkv, blk]
 };
+inline size_t score_counter_bytes(int B) { return ((size_t)B * sizeof(int) + 255) & ~(size_t)255; }
 size_t score_workspace_bytes(int B, int blk, int Hkv);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 

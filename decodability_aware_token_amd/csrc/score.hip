@@ -3,14 +3,15 @@
 // block's keys).  Project page "FOCUS: DLLMs Know How to Tame Their Compute Bound", Overview
 // cards "Design" and "Decodability Signal"; the paper's abstract (attention-derived importance).
 //
-// Kernel 1 (score_partial): one workgroup per (request r, kv head g), 4 waves.  For each layer
+// One workgroup per (request r, kv head g), 4 waves.  For each layer
 // the K tile of kv head g and the Q tiles of GS of its query heads are staged in LDS with
 // coalesced 16-byte loads, all issued before the LDS writes, with the next pass in flight.  A wave takes one (query head, 16-query tile) unit at a time and
 // computes S^T = K Q^T (keys x queries) on MFMA, so a lane holds one query's scores for 4 keys
 // of each 16-key tile: the row softmax over keys needs a local reduction plus two cross-lane
 // steps, and the column sums accumulate in registers across units and both layers (layer 0
 // subtracts, layer 1 adds).  The 16 query lanes are summed once at the end, the 4 waves in LDS
-// in a fixed order.  Kernel 2 (score_reduce) sums the Hkv partials in kv-head order.
+// in a fixed order; the last of a request's Hkv workgroups to finish sums their partials in
+// kv-head order (an arrival counter per request), so the result is deterministic.
 #include "device_common.h"
 #include "launch.h"
 
@@ -143,7 +144,9 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
                                                             const T* __restrict__ q1,
                                                             const T* __restrict__ k1, int Hq,
                                                             int Hkv, float scale_log2,
-                                                            float* __restrict__ part) {
+                                                            float* __restrict__ part,
+                                                            int* __restrict__ counters,
+                                                            float* __restrict__ delta) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int ROW = D + 16 / sizeof(T);
   constexpr int NMT = BLK / 16;
@@ -193,21 +196,30 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
       if (n16 == 0) red[wave * BLK + 16 * mt + 4 * j4 + i] = v;
     }
   __syncthreads();
-  if (tid < BLK)
-    part[(size_t)blockIdx.x * BLK + tid] =
-        ((red[tid] + red[BLK + tid]) + red[2 * BLK + tid]) + red[3 * BLK + tid];
-}
-
-__global__ __launch_bounds__(256) void score_reduce_kernel(const float* __restrict__ part, int B,
-                                                           int blk, int Hkv,
-                                                           float* __restrict__ delta) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= B * blk) return;
-  const int r = idx / blk, j = idx % blk;
-  const float* p = part + (size_t)r * Hkv * blk + j;
-  float s = 0.f;
-  for (int g = 0; g < Hkv; ++g) s += p[(size_t)g * blk];
-  delta[idx] = s;
+  // The Hkv workgroups of request r meet through an arrival counter: each stores its partial
+  // with device-scope stores (coherent across the XCDs' L2s), waits for them, and arrives; the
+  // last one sums the Hkv partials in kv-head order and resets the counter for the next call.
+  __shared__ int s_last;
+  if (tid < BLK) {
+    const float v = ((red[tid] + red[BLK + tid]) + red[2 * BLK + tid]) + red[3 * BLK + tid];
+    __hip_atomic_store(part + (size_t)blockIdx.x * BLK + tid, v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(counters + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             Hkv - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid < BLK) {
+    const float* pr = part + (size_t)r * Hkv * BLK + tid;
+    float sum = 0.f;
+    for (int gg = 0; gg < Hkv; ++gg)
+      sum += __hip_atomic_load(pr + (size_t)gg * BLK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    delta[(size_t)r * BLK + tid] = sum;
+  }
+  if (tid == 0) __hip_atomic_store(counters + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int BLK, int D, int GS>
@@ -216,11 +228,7 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
   const size_t shmem = (size_t)BLK * (1 + GS) * ROW * sizeof(T) + 4 * BLK * sizeof(float);
   hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS>), dim3(a.B * a.Hkv), dim3(256), shmem,
                      s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1, a.Hq,
-                     a.Hkv, a.scale_log2, a.part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(score_reduce_kernel, dim3((a.B * a.blk + 255) / 256), dim3(256), 0, s,
-                     a.part, a.B, a.blk, a.Hkv, a.delta);
+                     a.Hkv, a.scale_log2, a.part, a.counters, a.delta);
   return hipGetLastError();
 }
 
@@ -253,7 +261,7 @@ hipError_t launch_dt(const ScoreArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t score_workspace_bytes(int B, int blk, int Hkv) {
-  return (size_t)B * Hkv * blk * sizeof(float);
+  return score_counter_bytes(B) + (size_t)B * Hkv * blk * sizeof(float);
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {

@@ -3,6 +3,9 @@
 `FocusStep` preallocates every output and workspace once for a fixed batch shape, then `run()`
 issues the four C-ABI calls back to back on the current stream with no host synchronisation:
 ragged sizes stay on the device, and the attention is sized by the host-known bound max_kept.
+`capture()` records one step into a HIP graph (no allocation, no memset node: the kernels reset
+their own arrival counters), and `replay()` launches it, which removes the per-kernel launch
+gaps of the eager path.
 """
 from __future__ import annotations
 
@@ -58,7 +61,7 @@ class FocusStep:
         self.lse = torch.empty((max(self.cap, 1), Hq), dtype=torch.float32, device=dev) \
             if want_lse else None
         nsc = F.lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
-        self.ws_score = torch.empty(max(nsc, 1), dtype=torch.uint8, device=dev)
+        self.ws_score = torch.zeros(max(nsc, 1), dtype=torch.uint8, device=dev)
         S = inp.k_cache.shape[3]
         nat = F.attn_workspace_bytes(B, blk, Hq, Hkv, d, S, inp.page_table.shape[1], inp.max_kept)
         self.ws_attn = torch.zeros(max(nat, 1), dtype=torch.uint8, device=dev)  # zeros once
@@ -93,3 +96,18 @@ class FocusStep:
         self.compact_hidden()
         self.compact_q()
         self.attend()
+
+    def capture(self):
+        """Record one step into a HIP graph; the buffers above are its fixed inputs/outputs."""
+        side = torch.cuda.Stream(device=self.inp.q_att.device)  # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()  # the library's one-time queries happen outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        return self.graph
+
+    def replay(self):
+        self.graph.replay()

@@ -61,8 +61,10 @@ int focus_version(void);
  *   k0, k1      [B, blk, Hkv, d]  layer-0 / layer-1 block keys,    dtype `dtype`
  *   dtype       FOCUS_F32 or FOCUS_BF16 (products accumulate in f32)
  *   delta       [B, blk] f32 output
- *   workspace   device scratch of at least focus_score_l01_workspace_size(...) bytes
- *               (may be NULL when that size is 0); contents need no initialisation
+ *   workspace   device scratch of at least focus_score_l01_workspace_size(...) bytes,
+ *               ZERO-FILLED before its first use (it holds per-request arrival counters that
+ *               every call leaves at zero again, plus per-kv-head partial sums); calls that share
+ *               a workspace must not run concurrently
  * Supported: blk in {16,32,64}; d in {64,128}; Hq % Hkv == 0; Hq/Hkv in {1,2,4,8};
  *            1 <= B <= 4096; Hkv <= 64.  Pointers must be 16-byte aligned.
  * ------------------------------------------------------------------------------------------ */
@@ -109,8 +111,8 @@ int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t
  *   rows        [B, blk, row_bytes] bytes, or NULL (then gathered must be NULL: offsets only)
  *   offsets     [B+1] i32 output        kept_pos [cap] i32 output (may be NULL)
  *   gathered    [cap, row_bytes] output, or NULL
- * Supported: blk in {16,32,64}; 1 <= B <= 4096; row_bytes > 0 and a multiple of 16; rows and
- *            gathered 16-byte aligned; keep 4-byte aligned.
+ * Supported: blk in {16,32,64}; 1 <= B <= 4096; row_bytes > 0, a multiple of 16 and at most
+ *            2^24; rows and gathered 16-byte aligned; keep 4-byte aligned.
  * ------------------------------------------------------------------------------------------ */
 int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
                   int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,

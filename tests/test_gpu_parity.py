@@ -363,3 +363,26 @@ def test_attn_shared_workspace_across_calls():
             oerr = np.abs(out[:T].float().cpu().numpy() - ref_out).max()
             lerr = np.abs(lse[:T].cpu().numpy() - ref_lse).max()
             assert oerr <= OUT_TOL and lerr <= LSE_TOL, (case, oerr, lerr)
+
+
+def test_step_graph_replay_matches_eager():
+    # the whole step captured in a HIP graph: every replay, with eager work of the program in
+    # between, must reproduce the eager step bit for bit (the kernels reset their own counters)
+    _announce("graph replay")
+    st = make_step(BY_NAME["sdar_b256_blk32"].scaled(B=24))
+    fs, ref = run_gpu_step(st)
+    from parity_helpers import fetch
+    fs.capture()
+    for rep in range(3):
+        for name in ("out", "lse", "delta", "q_rows", "hidden_rows"):
+            t = getattr(fs, name)
+            if t is not None:
+                t.fill_(0)
+        torch.cuda.synchronize()
+        fs.replay()
+        torch.cuda.synchronize()
+        got = fetch(fs)
+        for key in ("delta", "keep", "offsets", "kept_pos", "out_bits", "lse", "hidden_rows"):
+            assert np.array_equal(got[key], ref[key]), (rep, key)
+        fs.run()  # eager work between replays
+        torch.cuda.synchronize()
