@@ -198,6 +198,34 @@ def summarize_profiles(out_root, workload):
     print("\n".join(lines + txt))
 
 
+def full_block_pass(inp, st, args, stream):
+    """The unfocused baseline on the same kernels (every block token a query), timed like the
+    focused step: its attention launch by HIP events, the step by graph replays."""
+    import torch
+    from decodability_aware_token_amd import FullBlockStep
+    fb = FullBlockStep(inp)
+    for _ in range(args.warmup):
+        fb.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fb.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = e0.elapsed_time(e1) / args.steps
+    kept = np.full(st.B, st.blk)
+    nbytes, flops = attn_algorithmic(st, kept)
+    rows = st.B * st.blk
+    log(f"[bench] full-block step: attention over {rows} rows {attn_ms * 1000:.1f} us, "
+        f"{nbytes / (attn_ms * 1e-3) / 1e9:.0f} GB/s, {flops / (attn_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    return {"rows": rows, "attn_us": round(attn_ms * 1000, 2),
+            "block_tokens_per_s": rows / (attn_ms * 1e-3),
+            "attn_algorithmic_bytes": nbytes, "attn_flops": flops,
+            "attn_hbm_frac": round(nbytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "attn_mfma_frac": round(flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +233,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdar_b256_blk32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-block", action="store_true",
+                    help="skip the unfocused (every block token kept) comparison step")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager launches instead of HIP graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -319,6 +349,10 @@ def main():
     log(f"[bench] score {sb / 1e6:.1f} MB -> {sb / (sc_ms * 1e-3) / 1e9:.0f} GB/s, "
         f"{sf / (sc_ms * 1e-3) / 1e12:.2f} TFLOP/s")
 
+    full = None
+    if not args.no_full_block:
+        full = full_block_pass(inp, st, args, stream)
+
     res = {
         "metric": "focused block-tokens/s per diffusion step",
         "value": T / (ms_per_step * 1e-3),
@@ -340,6 +374,7 @@ def main():
             "block_tokens_per_s": st.B * st.blk / (ms_per_step * 1e-3),
             "stage_us": {n: round(per_stage[j] * 1000, 2) for j, n in enumerate(stages)},
             "step_launch": mode, "eager_ms_per_step": round(eager_ms, 5),
+            "full_block_step": full,
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -111,3 +111,34 @@ class FocusStep:
 
     def replay(self):
         self.graph.replay()
+
+
+class FullBlockStep:
+    """The unfocused baseline on the same kernels: every block token is a query (k_r = blk), so
+    no scoring, selection or gather is needed -- the block queries [B, blk, Hq, d] already are
+    the ragged row list with offsets r * blk -- and the ragged paged attention runs on all of
+    them.  Project page "FOCUS: DLLMs Know How to Tame Their Compute Bound", card "Motivation"
+    (block diffusion recomputes the full block at every step)."""
+
+    def __init__(self, inp: StepInputs, want_lse: bool = True):
+        B, blk, Hq, d = inp.q_att.shape
+        dev = inp.q_att.device
+        self.inp = inp
+        self.B, self.blk = B, blk
+        self.q = inp.q_att.view(B * blk, Hq, d)
+        self.offsets = torch.arange(0, (B + 1) * blk, blk, dtype=torch.int32, device=dev)
+        self.out = torch.empty((B * blk, Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B * blk, Hq), dtype=torch.float32, device=dev) \
+            if want_lse else None
+        S = inp.k_cache.shape[3]
+        Hkv = inp.k_blk.shape[1]
+        nat = F.attn_workspace_bytes(B, blk, Hq, Hkv, d, S, inp.page_table.shape[1], blk)
+        self.ws_attn = torch.zeros(max(nat, 1), dtype=torch.uint8, device=dev)  # zeros once
+
+    def attend(self):
+        i = self.inp
+        F.ragged_paged_attn(self.q, self.offsets, i.k_cache, i.v_cache, i.page_table,
+                            i.prefix_len, i.k_blk, i.v_blk, self.blk, i.sm_scale, out=self.out,
+                            lse=self.lse, want_lse=self.lse is not None, workspace=self.ws_attn)
+
+    run = attend

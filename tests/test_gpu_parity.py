@@ -386,3 +386,25 @@ def test_step_graph_replay_matches_eager():
             assert np.array_equal(got[key], ref[key]), (rep, key)
         fs.run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,over", [("sdar_b256_blk32", {"B": 6}),
+                                       ("sweep_b128_blk64", {"B": 3}),
+                                       ("longctx_b64_blk32", {"B": 2})])
+def test_full_block_step(name, over):
+    # the unfocused baseline: every block token is a query (k_r = blk), rows = G * blk per kv
+    # head, so several query groups per item
+    from decodability_aware_token_amd import FullBlockStep
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"full-block step {name} {over}")
+    keep = np.ones((st.B, st.blk), dtype=np.uint8)
+    c = attn_case_inputs(st, keep)
+    ref_out, ref_lse = oracle_attention(st, c["q_rows64"], c["offsets"])
+    fb = FullBlockStep(step_inputs(st))
+    fb.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(fb.offsets.cpu().numpy(), c["offsets"])
+    oerr = np.abs(fb.out.float().cpu().numpy() - ref_out).max()
+    lerr = np.abs(fb.lse.cpu().numpy() - ref_lse).max()
+    assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
+    print(f"rows={st.B * st.blk} out err {oerr:.2e} lse err {lerr:.2e}")
