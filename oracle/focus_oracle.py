@@ -84,6 +84,53 @@ def score_l01(q0, k0, q1, k1, sm_scale: float, dtype: str = "bf16") -> np.ndarra
     return i1 - i0
 
 
+def prefix_keys(r: int, g: int, k_cache, page_table, prefix_len) -> np.ndarray:
+    """The prefix keys of request r for kv head g, in token order: [P, d] float64.  Token t is
+    in page page_table[r, t // S] at slot t % S; paged K layout [pages, Hkv, d/8, S, 8]."""
+    S = k_cache.shape[3]
+    d = k_cache.shape[2] * 8
+    P = int(prefix_len[r])
+    t = np.arange(P)
+    page = np.asarray(page_table[r], dtype=np.int64)[t // S]
+    return k_cache[page, g, :, t % S, :].reshape(P, d)
+
+
+def layer_importance_full(q: np.ndarray, k: np.ndarray, k_cache, page_table, prefix_len,
+                          sm_scale: float) -> np.ndarray:
+    """Attention mass each block token receives in one early layer, full attention domain.
+
+    The other reading of [PP, "Design"] (importance from the early layers' attention): a block
+    query's softmax runs over all keys it attends to in that layer -- the request's prefix keys
+    (from the paged cache of that layer) followed by the block keys -- and block token j's
+    importance is the weight it receives there, summed over query heads and block queries.
+    q: [B, blk, Hq, d], k: [B, blk, Hkv, d] float64 (the layer's block Q/K); k_cache float64 in
+    the paged layout.  Returns I [B, blk].
+    """
+    B, blk, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    imp = np.zeros((B, blk), dtype=np.float64)
+    for r in range(B):
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([prefix_keys(r, g, k_cache, page_table, prefix_len),
+                                   k[r, :, g, :]], axis=0)                  # [P + blk, d]
+            s = sm_scale * (q[r, :, h, :] @ keys.T)                          # [blk, P + blk]
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)                             # over all keys
+            imp[r] += p[:, keys.shape[0] - blk:].sum(axis=0)                 # block columns
+    return imp
+
+
+def score_l01_full(q0, k0, q1, k1, k_cache0, k_cache1, page_table, prefix_len,
+                   sm_scale: float) -> np.ndarray:
+    """delta = I_1 - I_0 with the full-domain importance of each layer (layer l's prefix keys
+    in k_cache_l).  Inputs float64 (bf16 widened exactly)."""
+    return (layer_importance_full(q1, k1, k_cache1, page_table, prefix_len, sm_scale)
+            - layer_importance_full(q0, k0, k_cache0, page_table, prefix_len, sm_scale))
+
+
 # --------------------------------------------------------------------------------------------
 # a2: budgeted selection
 # --------------------------------------------------------------------------------------------

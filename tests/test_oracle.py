@@ -116,6 +116,111 @@ def test_importance_against_torch_softmax():
     np.testing.assert_allclose(imp, p.sum(dim=(1, 2)).numpy(), atol=1e-12)
 
 
+# ------------------------------------------------------------------ full-domain scoring
+def _paged_prefix(rng, B, Hkv, d, S, plen, scale=1.0):
+    """Random prefix keys per request, stored sequentially in pages; returns (k_cache float64
+    in the paged layout, page_table, dense keys per request [P, Hkv, d])."""
+    npg = [(-(-int(P) // S)) for P in plen]
+    tot = max(sum(npg), 1)
+    dense = rng.standard_normal((tot * S, Hkv, d)) * scale
+    table = np.full((B, max(max(npg), 1)), -1, dtype=np.int32)
+    base, keys = 0, []
+    for r in range(B):
+        table[r, : npg[r]] = np.arange(base, base + npg[r])
+        keys.append(dense[base * S: base * S + int(plen[r])])
+        base += npg[r]
+    return pack_k(dense, S), table, keys
+
+
+def test_full_domain_importance_without_prefix_is_block_only():
+    # with no prefix key the full domain is the block: the two readings coincide
+    rng = np.random.default_rng(21)
+    B, blk, Hq, Hkv, d, S = 3, 16, 4, 2, 8, 16
+    q = rng.standard_normal((B, blk, Hq, d))
+    k = rng.standard_normal((B, blk, Hkv, d))
+    kc, table, _ = _paged_prefix(rng, B, Hkv, d, S, [0, 0, 0])
+    full = O.layer_importance_full(q, k, kc, table, np.zeros(B, np.int32), 0.4)
+    np.testing.assert_allclose(full, O.layer_importance(q, k, 0.4), rtol=0, atol=1e-12)
+
+
+def test_full_domain_importance_matches_torch_softmax_over_prefix_and_block():
+    # an independent float64 torch.softmax over [prefix keys; block keys] per (r, h), read
+    # through the page table, then the block columns summed over the queries
+    rng = np.random.default_rng(22)
+    B, blk, Hq, Hkv, d, S = 2, 16, 4, 2, 8, 16
+    plen = np.array([37, 5], dtype=np.int32)
+    q = rng.standard_normal((B, blk, Hq, d))
+    k = rng.standard_normal((B, blk, Hkv, d))
+    kc, table, keys = _paged_prefix(rng, B, Hkv, d, S, plen)
+    got = O.layer_importance_full(q, k, kc, table, plen, 0.35)
+    ref = np.zeros((B, blk))
+    for r in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            allk = torch.from_numpy(np.concatenate([keys[r][:, g, :], k[r, :, g, :]]))
+            z = 0.35 * torch.from_numpy(q[r, :, h, :]) @ allk.T
+            ref[r] += torch.softmax(z, dim=1)[:, plen[r]:].sum(dim=0).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_full_domain_importance_duplicate_prefix_key_closed_form():
+    # one prefix token equal to block key 0: row i's full-domain weights are the block-only
+    # ones divided by 1 + p_i0 (the duplicate adds the weight of key 0 to the denominator)
+    rng = np.random.default_rng(23)
+    blk, Hq, Hkv, d, S = 16, 2, 1, 8, 16
+    q = rng.standard_normal((1, blk, Hq, d))
+    k = rng.standard_normal((1, blk, Hkv, d))
+    dense = np.zeros((S, Hkv, d))
+    dense[0] = k[0, 0]
+    kc = pack_k(dense, S)
+    got = O.layer_importance_full(q, k, kc, np.array([[0]], np.int32), np.array([1]), 0.5)
+    exp = np.zeros(blk)
+    for h in range(Hq):
+        z = 0.5 * q[0, :, h, :] @ k[0, :, 0, :].T
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        exp += (p / (1.0 + p[:, :1])).sum(axis=0)
+    np.testing.assert_allclose(got[0], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_full_domain_importance_is_below_block_only_and_mass_adds_up():
+    # a superset of keys only grows each row's denominator: every block key's weight shrinks;
+    # the block mass plus the prefix mass is Hq * blk
+    rng = np.random.default_rng(24)
+    B, blk, Hq, Hkv, d, S = 2, 32, 4, 4, 8, 16
+    plen = np.array([50, 17], dtype=np.int32)
+    q = rng.standard_normal((B, blk, Hq, d))
+    k = rng.standard_normal((B, blk, Hkv, d))
+    kc, table, keys = _paged_prefix(rng, B, Hkv, d, S, plen)
+    full = O.layer_importance_full(q, k, kc, table, plen, 0.3)
+    assert np.all(full <= O.layer_importance(q, k, 0.3) + 1e-12)
+    for r in range(B):
+        pm = 0.0
+        for h in range(Hq):
+            allk = np.concatenate([keys[r][:, h, :], k[r, :, h, :]])
+            z = 0.3 * q[r, :, h, :] @ allk.T
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            p = p / p.sum(axis=1, keepdims=True)
+            pm += p[:, : plen[r]].sum()
+        assert abs(full[r].sum() + pm - Hq * blk) < 1e-9
+
+
+def test_full_domain_score_is_layer_difference_with_own_caches():
+    # delta takes layer 1 minus layer 0, each with its own prefix cache: swapping the layers
+    # (inputs and caches together) negates it
+    rng = np.random.default_rng(25)
+    B, blk, Hq, Hkv, d, S = 2, 16, 4, 2, 8, 16
+    plen = np.array([20, 9], dtype=np.int32)
+    q0, q1 = rng.standard_normal((2, B, blk, Hq, d))
+    k0, k1 = rng.standard_normal((2, B, blk, Hkv, d))
+    kc0, table, _ = _paged_prefix(rng, B, Hkv, d, S, plen)
+    kc1 = pack_k(rng.standard_normal((kc0.shape[0] * S, Hkv, d)), S)
+    a = O.score_l01_full(q0, k0, q1, k1, kc0, kc1, table, plen, 0.3)
+    b = O.score_l01_full(q1, k1, q0, k0, kc1, kc0, table, plen, 0.3)
+    np.testing.assert_allclose(a, -b, rtol=0, atol=1e-12)
+    assert abs(a.sum()) > 1e-6
+
+
 # ------------------------------------------------------------------ selection
 def test_select_hand_example():
     delta = np.array([[0.1, 0.9, 0.5, 0.9, -0.2, 0.7, 0.0, 0.3]])
