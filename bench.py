@@ -226,6 +226,36 @@ def full_block_pass(inp, st, args, stream):
             "attn_mfma_frac": round(flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def full_domain_pass(inp, t, st, args, stream):
+    """Importance over the full attention domain: the score kernel with each block query's
+    prefix+block log-sum-exp given (its own roofline), and the two layers' attentions that
+    produce those LSEs here (in a model they come with layers 0 and 1)."""
+    import torch
+    from decodability_aware_token_amd import FullDomainScore
+    fd = FullDomainScore(inp, t["k_cache0"], t["k_blk0"])
+    for _ in range(args.warmup):
+        fd.run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        fd.layer_lse()
+    ev[1].record(stream)
+    for _ in range(args.steps):
+        fd.score()
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    lse_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    sc_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    sb, sf = score_algorithmic(st)
+    sb += 2 * st.B * st.blk * st.Hq * 4  # the two LSE arrays
+    log(f"[bench] full-domain score: {sc_ms * 1000:.1f} us ({sb / (sc_ms * 1e-3) / 1e9:.0f} GB/s); "
+        f"the two layers' LSE attentions {lse_ms * 1000:.1f} us")
+    return {"score_lse_us": round(sc_ms * 1000, 2), "score_lse_algorithmic_bytes": sb,
+            "score_lse_hbm_frac": round(sb / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "layer_lse_attention_us": round(lse_ms * 1000, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +263,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdar_b256_blk32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-domain", action="store_true",
+                    help="skip the full-domain importance measurement")
     ap.add_argument("--no-full-block", action="store_true",
                     help="skip the unfocused (every block token kept) comparison step")
     ap.add_argument("--no-graph", action="store_true",
@@ -275,7 +307,7 @@ def main():
 
     recipe = BY_NAME[args.workload]
     log(f"[bench] generating {recipe.name}")
-    st = make_step(recipe)
+    st = make_step(recipe, layer0_prefix=not args.no_full_domain)
     dev = torch.device("cuda:0")
     t = upload(st, dev)
     inp = StepInputs(**{k: t[k] for k in ("q0", "k0", "q1", "k1", "masked", "budget", "adaptive",
@@ -352,6 +384,9 @@ def main():
     full = None
     if not args.no_full_block:
         full = full_block_pass(inp, st, args, stream)
+    fdom = None
+    if not args.no_full_domain:
+        fdom = full_domain_pass(inp, t, st, args, stream)
 
     res = {
         "metric": "focused block-tokens/s per diffusion step",
@@ -375,6 +410,7 @@ def main():
             "stage_us": {n: round(per_stage[j] * 1000, 2) for j, n in enumerate(stages)},
             "step_launch": mode, "eager_ms_per_step": round(eager_ms, 5),
             "full_block_step": full,
+            "full_domain_score": fdom,
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -7,6 +7,6 @@ step (``pipeline``).
 from .binding import (  # noqa: F401
     FocusError, compact, lib, ragged_paged_attn, score_l01, select_budget, status_string,
 )
-from .pipeline import FocusStep, FullBlockStep, StepInputs  # noqa: F401
+from .pipeline import FocusStep, FullBlockStep, FullDomainScore, StepInputs  # noqa: F401
 
 __version__ = "0.1.0"

@@ -34,6 +34,9 @@ SIGNATURES = {
     "focus_score_l01_workspace_size": (_c_size_t, [_c_int] * 5),
     "focus_score_l01": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p,
                                                                   _c_size_t, _c_void_p]),
+    "focus_score_l01_lse": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p,
+                                                                      _c_void_p, _c_size_t,
+                                                                      _c_void_p]),
     "focus_select_budget": (_c_int, [_c_void_p] * 3 + [_c_int, _c_float, _c_int, _c_int, _c_int,
                                                        _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "focus_compact": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int64, _c_int, _c_void_p,
@@ -116,6 +119,24 @@ def score_l01(q0, k0, q1, k1, sm_scale: float, delta=None, workspace=None) -> to
                                float(sm_scale), _ptr(delta), _ptr(workspace), wsb,
                                _stream(q0.device))
     _check("focus_score_l01", rc)
+    return delta
+
+
+def score_l01_lse(q0, k0, q1, k1, lse0, lse1, sm_scale: float, delta=None,
+                  workspace=None) -> torch.Tensor:
+    """delta [B, blk] f32 over the full attention domain, given each block query's log-sum-exp
+    over prefix + block keys per layer, lse_l [B, blk, Hq] f32 (see focus_score_l01_lse)."""
+    B, blk, Hq, d = q0.shape
+    Hkv = k0.shape[2]
+    dt = {torch.float32: FOCUS_F32, torch.bfloat16: FOCUS_BF16}[q0.dtype]
+    if delta is None:
+        delta = torch.empty((B, blk), dtype=torch.float32, device=q0.device)
+    need = lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
+    workspace, wsb = _workspace(need, q0.device, workspace)
+    rc = lib().focus_score_l01_lse(_ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), _ptr(lse0),
+                                   _ptr(lse1), dt, B, blk, Hq, Hkv, d, float(sm_scale),
+                                   _ptr(delta), _ptr(workspace), wsb, _stream(q0.device))
+    _check("focus_score_l01_lse", rc)
     return delta
 
 

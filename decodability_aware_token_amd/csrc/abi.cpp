@@ -49,9 +49,11 @@ size_t focus_score_l01_workspace_size(int B, int blk, int Hq, int Hkv, int d) {
   return focus::score_workspace_bytes(B, blk, Hkv);
 }
 
-int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* k1, int dtype,
-                    int B, int blk, int Hq, int Hkv, int d, float sm_scale, float* delta,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
+                 const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
+                 int Hkv, int d, float sm_scale, float* delta, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
   if (!q0 || !k0 || !q1 || !k1 || !delta) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FOCUS_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return FOCUS_ERR_INVALID_ARG;
@@ -61,6 +63,7 @@ int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* 
   if (!pow2_in(blk, 16, 64) || (d != 64 && d != 128) || B > kMaxB) return FOCUS_ERR_UNSUPPORTED;
   if (!aligned16(q0) || !aligned16(k0) || !aligned16(q1) || !aligned16(k1))
     return FOCUS_ERR_INVALID_ARG;
+  if (lse0 && (!aligned4(lse0) || !aligned4(lse1))) return FOCUS_ERR_INVALID_ARG;
   const size_t need = focus::score_workspace_bytes(B, blk, Hkv);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FOCUS_ERR_WORKSPACE;
   focus::ScoreArgs a{};
@@ -75,11 +78,30 @@ int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* 
   a.Hkv = Hkv;
   a.d = d;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.lse0 = lse0;
+  a.lse1 = lse1;
   a.delta = delta;
   a.counters = static_cast<int*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
                                     focus::score_counter_bytes(B));
   return status_of(focus::launch_score(a, stream));
+}
+}  // namespace
+
+int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* k1, int dtype,
+                    int B, int blk, int Hq, int Hkv, int d, float sm_scale, float* delta,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return score_common(q0, k0, q1, k1, nullptr, nullptr, dtype, B, blk, Hq, Hkv, d, sm_scale,
+                      delta, workspace, workspace_bytes, stream);
+}
+
+int focus_score_l01_lse(const void* q0, const void* k0, const void* q1, const void* k1,
+                        const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
+                        int Hkv, int d, float sm_scale, float* delta, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (!lse0 || !lse1) return FOCUS_ERR_INVALID_ARG;
+  return score_common(q0, k0, q1, k1, lse0, lse1, dtype, B, blk, Hq, Hkv, d, sm_scale, delta,
+                      workspace, workspace_bytes, stream);
 }
 
 int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t* budget,

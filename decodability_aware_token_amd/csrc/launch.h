@@ -16,6 +16,8 @@ struct ScoreArgs {
   int is_bf16;
   int B, blk, Hq, Hkv, d;
   float scale_log2;  // sm_scale * log2(e)
+  const float* lse0; // [B, blk, Hq] full-domain row log-sum-exp of layer 0, or null (block-only)
+  const float* lse1; // same for layer 1
   float* delta;      // [B, blk]
   int* counters;     // workspace [B] arrival counters (zero between calls)
   float* part;       // workspace [B, Hkv, blk]

@@ -73,11 +73,14 @@ __device__ __forceinline__ void store_pass(const Pass<T, BLK, D, GS>& ps, T* Ks,
 }
 
 // Column sums of the row softmax of S^T = K Q^T for one (query head, 16-query tile) unit,
-// accumulated into colacc with sign -1 (layer 0) or +1 (layer 1).
-template <typename T, int BLK, int D, int GS>
+// accumulated into colacc with sign -1 (layer 0) or +1 (layer 1).  Block-only domain: the row is
+// normalised over the BLK block keys.  Full domain (FULL): the row's log-sum-exp over prefix and
+// block keys is given (row_lse_log2, in log2 units, for this lane's query), and the block keys'
+// weights are exp2(z - row_lse_log2).
+template <typename T, int BLK, int D, int GS, bool FULL>
 __device__ __forceinline__ void score_unit(const T* Ks, const T* Qs, int hh, int nt, int n16,
                                            int j4, float scale_log2, float sign,
-                                           float (&colacc)[BLK / 16][4]) {
+                                           float row_lse_log2, float (&colacc)[BLK / 16][4]) {
   constexpr int ES = sizeof(T);
   constexpr int ROW = D + 16 / ES;
   constexpr int NMT = BLK / 16;
@@ -110,7 +113,16 @@ __device__ __forceinline__ void score_unit(const T* Ks, const T* Qs, int hh, int
         acc[mt] = mfma_f32(krow[4 * kk + j4], qrow[4 * kk + j4], acc[mt]);
     }
   }
-  // acc[mt][i] = S[key 16mt + 4*j4 + i][query 16nt + n16]; softmax over all BLK keys.
+  // acc[mt][i] = S[key 16mt + 4*j4 + i][query 16nt + n16]
+  if constexpr (FULL) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        colacc[mt][i] += sign * fast_exp2(acc[mt][i] * scale_log2 - row_lse_log2);
+    return;
+  }
+  // softmax over all BLK keys
   float mx = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
@@ -138,12 +150,14 @@ __device__ __forceinline__ void score_unit(const T* Ks, const T* Qs, int hh, int
 
 // Passes run (layer, head group) in order; the next pass's global loads are in flight (in
 // registers) while the current one is computed from LDS.
-template <typename T, int BLK, int D, int GS>
+template <typename T, int BLK, int D, int GS, bool FULL>
 __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict__ q0,
                                                             const T* __restrict__ k0,
                                                             const T* __restrict__ q1,
                                                             const T* __restrict__ k1, int Hq,
                                                             int Hkv, float scale_log2,
+                                                            const float* __restrict__ lse0,
+                                                            const float* __restrict__ lse1,
                                                             float* __restrict__ part,
                                                             int* __restrict__ counters,
                                                             float* __restrict__ delta) {
@@ -178,9 +192,18 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
       const int nl = (pi + 1) / groups, nh = ((pi + 1) % groups) * GS;
       load_pass<T, BLK, D, GS>(ps, nl ? q1 : q0, nl ? k1 : k0, r, g, Hq, Hkv, G, nh, tid);
     }
-    const float sign = (pi / groups) ? 1.f : -1.f;
-    for (int u = wave; u < GS * NMT; u += 4)
-      score_unit<T, BLK, D, GS>(Ks, Qs, u / NMT, u % NMT, n16, j4, scale_log2, sign, colacc);
+    const int layer = pi / groups, h0 = (pi % groups) * GS;
+    const float sign = layer ? 1.f : -1.f;
+    for (int u = wave; u < GS * NMT; u += 4) {
+      const int hh = u / NMT, nt = u % NMT;
+      float row_lse_log2 = 0.f;
+      if constexpr (FULL) {
+        const float* lse = layer ? lse1 : lse0;  // [B, BLK, Hq], natural log
+        row_lse_log2 = lse[((size_t)r * BLK + 16 * nt + n16) * Hq + g * G + h0 + hh] * kLog2e;
+      }
+      score_unit<T, BLK, D, GS, FULL>(Ks, Qs, hh, nt, n16, j4, scale_log2, sign, row_lse_log2,
+                                      colacc);
+    }
   }
 
   // Sum over the 16 query lanes of each lane group, then over the 4 waves.
@@ -226,9 +249,15 @@ template <typename T, int BLK, int D, int GS>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
   constexpr int ROW = D + 16 / sizeof(T);
   const size_t shmem = (size_t)BLK * (1 + GS) * ROW * sizeof(T) + 4 * BLK * sizeof(float);
-  hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS>), dim3(a.B * a.Hkv), dim3(256), shmem,
-                     s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1, a.Hq,
-                     a.Hkv, a.scale_log2, a.part, a.counters, a.delta);
+  if (a.lse0 != nullptr)
+    hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS, true>), dim3(a.B * a.Hkv), dim3(256),
+                       shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1,
+                       a.Hq, a.Hkv, a.scale_log2, a.lse0, a.lse1, a.part, a.counters, a.delta);
+  else
+    hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS, false>), dim3(a.B * a.Hkv),
+                       dim3(256), shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1,
+                       (const T*)a.k1, a.Hq, a.Hkv, a.scale_log2, nullptr, nullptr, a.part,
+                       a.counters, a.delta);
   return hipGetLastError();
 }
 

@@ -142,3 +142,49 @@ class FullBlockStep:
                             lse=self.lse, want_lse=self.lse is not None, workspace=self.ws_attn)
 
     run = attend
+
+
+class FullDomainScore:
+    """Importance over the full attention domain (prefix + block keys) of layers 0 and 1: each
+    layer's ragged paged attention runs on every block query (rows r*blk + i) over that layer's
+    prefix cache and block keys, and its log-sum-exp output normalises the block keys' weights in
+    focus_score_l01_lse.  Project page "FOCUS: DLLMs Know How to Tame Their Compute Bound", card
+    "Design" (importance from the early layers' attention).  In a model the two LSEs come with
+    the layers' own attention; here they are computed with the same attention kernel.  V does
+    not enter a log-sum-exp, so both layers' attentions read the one value cache given."""
+
+    def __init__(self, inp: StepInputs, k_cache0: torch.Tensor, k_blk0: torch.Tensor):
+        B, blk, Hq, d = inp.q_att.shape
+        dev = inp.q_att.device
+        self.inp, self.k_cache0, self.k_blk0 = inp, k_cache0, k_blk0
+        self.B, self.blk, self.Hq, self.d = B, blk, Hq, d
+        self.offsets = torch.arange(0, (B + 1) * blk, blk, dtype=torch.int32, device=dev)
+        self.out = torch.empty((B * blk, Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse0 = torch.empty((B * blk, Hq), dtype=torch.float32, device=dev)
+        self.lse1 = torch.empty((B * blk, Hq), dtype=torch.float32, device=dev)
+        self.delta = torch.empty((B, blk), dtype=torch.float32, device=dev)
+        S = inp.k_cache.shape[3]
+        Hkv = inp.k_blk.shape[1]
+        nat = F.attn_workspace_bytes(B, blk, Hq, Hkv, d, S, inp.page_table.shape[1], blk)
+        self.ws_attn = torch.zeros(max(nat, 1), dtype=torch.uint8, device=dev)
+        nsc = F.lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
+        self.ws_score = torch.zeros(max(nsc, 1), dtype=torch.uint8, device=dev)
+
+    def layer_lse(self):
+        i = self.inp
+        for q, kc, kb, lse in ((i.q0, self.k_cache0, self.k_blk0, self.lse0),
+                               (i.q1, i.k_cache, i.k_blk, self.lse1)):
+            F.ragged_paged_attn(q.reshape(self.B * self.blk, self.Hq, self.d), self.offsets, kc,
+                                i.v_cache, i.page_table, i.prefix_len, kb, i.v_blk, self.blk,
+                                i.sm_scale, out=self.out, lse=lse, workspace=self.ws_attn)
+
+    def score(self):
+        i = self.inp
+        F.score_l01_lse(i.q0, i.k0, i.q1, i.k1, self.lse0.view(self.B, self.blk, self.Hq),
+                        self.lse1.view(self.B, self.blk, self.Hq), i.sm_scale, delta=self.delta,
+                        workspace=self.ws_score)
+
+    def run(self):
+        self.layer_lse()
+        self.score()
+        return self.delta

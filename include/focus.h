@@ -74,6 +74,27 @@ int focus_score_l01(const void* q0, const void* k0, const void* q1, const void* 
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------------
+ * 1b. Importance scoring over the full attention domain.
+ *
+ * The other reading of the importance in call 1 (project page, card "Design": importance from
+ * the early layers' attention): the softmax of each block query runs over the layer's whole key
+ * set -- the request's prefix tokens and the block -- and a block token's importance is the
+ * weight it receives there:
+ *     P = exp( sm_scale * q_l[r,i,h,:] . k_l[r,j,g,:] - lse_l[r,i,h] )    (block keys j only)
+ *     I_l[r,j] = sum_h sum_i P,   delta[r,j] = I_1[r,j] - I_0[r,j]
+ * lse_l[r,i,h] is the natural-log log-sum-exp of sm_scale * q . k over all keys (prefix and
+ * block) of layer l, e.g. the `lse` output of focus_ragged_paged_attn run on every block query
+ * of that layer (rows r*blk + i).  The prefix keys themselves are not read.
+ *
+ *   lse0, lse1  [B, blk, Hq] f32 (4-byte aligned), device memory
+ *   everything else as in focus_score_l01 (same workspace size and rules, same supported set)
+ * ------------------------------------------------------------------------------------------ */
+int focus_score_l01_lse(const void* q0, const void* k0, const void* q1, const void* k1,
+                        const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
+                        int Hkv, int d, float sm_scale, float* delta, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
  * 2. Budgeted selection (target token selection).
  *
  * Defined by the project page, cards "Design" (keep likely-decodable candidates under an

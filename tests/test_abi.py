@@ -71,6 +71,25 @@ def test_score_errors():
     assert _score(wsb=need - 1) == F.FOCUS_ERR_WORKSPACE
 
 
+def _score_lse(**kw):
+    a = dict(q0=P, k0=P, q1=P, k1=P, l0=P, l1=P, dt=1, B=4, blk=32, Hq=32, Hkv=8, d=128, sc=0.1,
+             delta=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return F.lib().focus_score_l01_lse(a["q0"], a["k0"], a["q1"], a["k1"], a["l0"], a["l1"],
+                                       a["dt"], a["B"], a["blk"], a["Hq"], a["Hkv"], a["d"],
+                                       a["sc"], a["delta"], a["ws"], a["wsb"], None)
+
+
+def test_score_lse_errors():
+    # the full-domain variant validates like focus_score_l01 and needs both row LSE arrays
+    assert _score_lse(l0=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _score_lse(l1=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _score_lse(l0=P + 2) == F.FOCUS_ERR_INVALID_ARG   # misaligned
+    assert _score_lse(q0=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _score_lse(blk=24) == F.FOCUS_ERR_UNSUPPORTED
+    assert _score_lse(ws=None) == F.FOCUS_ERR_WORKSPACE
+
+
 def _select(**kw):
     a = dict(delta=P, masked=P, budget=P, ad=0, beta=0.5, lo=2, hi=16, B=4, blk=32, keep=P,
              kept=P)

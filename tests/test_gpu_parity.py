@@ -408,3 +408,41 @@ def test_full_block_step(name, over):
     lerr = np.abs(fb.lse.cpu().numpy() - ref_lse).max()
     assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
     print(f"rows={st.B * st.blk} out err {oerr:.2e} lse err {lerr:.2e}")
+
+
+FULL_DOMAIN_CASES = {"sdar_b32_blk32": {"B": 4}, "longctx_b64_blk32": {"B": 2},
+                     "sweep_b128_blk16": {"B": 3}}
+
+
+@pytest.mark.parametrize("name", list(FULL_DOMAIN_CASES))
+def test_full_domain_score(name):
+    # layer-0/1 attentions over every block query give the row LSEs; the score variant then
+    # weights block keys by exp(z - lse): compared with the oracle's softmax over prefix+block
+    from decodability_aware_token_amd import FullDomainScore
+    st = make_step(BY_NAME[name].scaled(**FULL_DOMAIN_CASES[name]), layer0_prefix=True)
+    _announce(f"full-domain score {name} B={st.B} S={st.S}")
+    f64 = O.bf16_to_f64
+    ref = O.score_l01_full(f64(st.q0), f64(st.k0), f64(st.q1), f64(st.k1), f64(st.k_cache0),
+                           f64(st.k_cache), st.page_table, st.prefix_len, st.sm_scale)
+    from workloads.torch_io import upload
+    t = upload(st)
+    fd = FullDomainScore(step_inputs(st), t["k_cache0"], t["k_blk0"])
+    got = fd.run()
+    torch.cuda.synchronize()
+    err = np.abs(got.cpu().numpy() - ref).max()
+    assert err <= DELTA_TOL, err
+    # the score call alone, fed the oracle's own row LSEs
+    offs = np.arange(st.B + 1, dtype=np.int32) * st.blk
+    rows0 = f64(st.q0).reshape(-1, st.Hq, st.d)
+    rows1 = f64(st.q1).reshape(-1, st.Hq, st.d)
+    _, l0 = O.ragged_paged_attn(rows0, offs, f64(st.k_cache0), f64(st.v_cache), st.page_table,
+                                st.prefix_len, f64(st.k_blk0), f64(st.v_blk), st.sm_scale)
+    _, l1 = O.ragged_paged_attn(rows1, offs, f64(st.k_cache), f64(st.v_cache), st.page_table,
+                                st.prefix_len, f64(st.k_blk), f64(st.v_blk), st.sm_scale)
+    lse0 = torch.from_numpy(l0.astype(np.float32).reshape(st.B, st.blk, st.Hq)).cuda()
+    lse1 = torch.from_numpy(l1.astype(np.float32).reshape(st.B, st.blk, st.Hq)).cuda()
+    got2 = F.score_l01_lse(t["q0"], t["k0"], t["q1"], t["k1"], lse0, lse1, st.sm_scale)
+    torch.cuda.synchronize()
+    err2 = np.abs(got2.cpu().numpy() - ref).max()
+    assert err2 <= DELTA_TOL, err2
+    print(f"delta err {err:.2e} (own LSE), {err2:.2e} (oracle LSE)")

@@ -95,6 +95,8 @@ class Step:
     v_cache: np.ndarray           # [num_pages, Hkv, S/8, d, 8] uint16
     hidden: Optional[np.ndarray]  # [B, blk, W] uint16 or None
     bias_pos: Optional[np.ndarray] = None
+    k_cache0: Optional[np.ndarray] = None  # layer-0 prefix keys, paged like k_cache (optional)
+    k_blk0: Optional[np.ndarray] = None    # layer-0 block keys, packed like k_blk (optional)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -139,13 +141,15 @@ def _draw_normal(seed: int, stream: int, shape, scale: float, bf16: bool) -> np.
 
 def make_step(recipe: Recipe, seed: Optional[int] = None, poison: bool = False,
               prefix_override: Optional[np.ndarray] = None,
-              masked_override: Optional[np.ndarray] = None) -> Step:
+              masked_override: Optional[np.ndarray] = None, layer0_prefix: bool = False) -> Step:
     """Draw one synthetic step for ``recipe``.
 
     ``poison`` fills every memory location the step must never read (cache slots past a prefix,
     spare pool pages, page-table entries past a request's last page) with NaN / out-of-range ids.
     ``prefix_override`` / ``masked_override`` replace the drawn prefix lengths / masked counts
     (edge-case tests); the random stream is consumed identically either way.
+    ``layer0_prefix`` also draws the layer-0 prefix keys (stream 10) into their own paged cache
+    with the same page table, and packs the layer-0 block keys, for the full-domain importance.
     """
     r = recipe
     rng = np.random.Generator(np.random.PCG64(r.seed if seed is None else seed))
@@ -239,27 +243,35 @@ def make_step(recipe: Recipe, seed: Optional[int] = None, poison: bool = False,
 
     # 7. scatter prefix tokens into pages (slots past a prefix are zero, or NaN when poisoned)
     fill = BF16_NAN if poison else np.uint16(0)
-    k_cache = np.full((pool, Hkv, d // 8, S, 8), fill, dtype=np.uint16)
-    v_cache = np.full((pool, Hkv, S // 8, d, 8), fill, dtype=np.uint16)
     tstart = np.concatenate([[0], np.cumsum(plen)])
-    for b in range(B):
-        n = int(plen[b])
-        if n == 0:
-            continue
-        nfull = n // S
-        ids = table[b, : npg[b]].astype(np.int64)
-        if nfull:
-            k_cache[ids[:nfull]] = pack_k(pk[tstart[b]: tstart[b] + nfull * S], S)
-            v_cache[ids[:nfull]] = pack_v(pv[tstart[b]: tstart[b] + nfull * S], S)
-        rem = n - nfull * S
-        if rem:
-            tail_k = np.full((S, Hkv, d), fill, dtype=np.uint16)
-            tail_v = np.full((S, Hkv, d), fill, dtype=np.uint16)
-            tail_k[:rem] = pk[tstart[b] + nfull * S: tstart[b] + n]
-            tail_v[:rem] = pv[tstart[b] + nfull * S: tstart[b] + n]
-            k_cache[ids[nfull]] = pack_k(tail_k, S)[0]
-            v_cache[ids[nfull]] = pack_v(tail_v, S)[0]
+
+    def paged(tokens, shape, pack):
+        cache = np.full((pool,) + shape, fill, dtype=np.uint16)
+        for b in range(B):
+            n = int(plen[b])
+            if n == 0:
+                continue
+            nfull = n // S
+            ids = table[b, : npg[b]].astype(np.int64)
+            if nfull:
+                cache[ids[:nfull]] = pack(tokens[tstart[b]: tstart[b] + nfull * S], S)
+            rem = n - nfull * S
+            if rem:
+                tail = np.full((S, Hkv, d), fill, dtype=np.uint16)
+                tail[:rem] = tokens[tstart[b] + nfull * S: tstart[b] + n]
+                cache[ids[nfull]] = pack(tail, S)[0]
+        return cache
+
+    k_cache = paged(pk, (Hkv, d // 8, S, 8), pack_k)
+    v_cache = paged(pv, (Hkv, S // 8, d, 8), pack_v)
     del pk, pv
+    k_cache0 = k_blk0 = None
+    if layer0_prefix:
+        pk0 = _draw_normal(seed_, 10, (total, Hkv, d), sc, True)
+        k_cache0 = paged(pk0, (Hkv, d // 8, S, 8), pack_k)
+        del pk0
+        k0_16 = f32_to_bf16_bits(k0) if f32 else k0
+        k_blk0 = pack_k(k0_16.reshape(B * blk, Hkv, d), blk)
     s_q0, s_k0, s_q1, s_k1 = q0, k0, q1, k1
 
     rule = ("fixed",)
@@ -277,4 +289,5 @@ def make_step(recipe: Recipe, seed: Optional[int] = None, poison: bool = False,
                 budget=budget, rule=rule, max_kept=r.max_kept(),
                 prefix_len=plen.astype(np.int32), page_table=table, num_pages=pool,
                 q0=s_q0, k0=s_k0, q1=s_q1, k1=s_k1, q_att=q_att, k_blk=k_blk, v_blk=v_blk,
-                k_cache=k_cache, v_cache=v_cache, hidden=hidden, bias_pos=bias_pos)
+                k_cache=k_cache, v_cache=v_cache, hidden=hidden, bias_pos=bias_pos,
+                k_cache0=k_cache0, k_blk0=k_blk0)

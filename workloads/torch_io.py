@@ -36,5 +36,7 @@ def upload(st, device="cuda"):
         "v_blk": bf16_tensor(st.v_blk, device),
         "sm_scale": float(st.sm_scale),
         "hidden": None if st.hidden is None else bf16_tensor(st.hidden, device),
+        "k_cache0": None if st.k_cache0 is None else bf16_tensor(st.k_cache0, device),
+        "k_blk0": None if st.k_blk0 is None else bf16_tensor(st.k_blk0, device),
     }
     return d
