@@ -295,6 +295,74 @@ def ragged_paged_attn(q: np.ndarray, offsets: np.ndarray, k_cache, v_cache, page
 
 
 # --------------------------------------------------------------------------------------------
+# f3: intra-block KV write-back and block commit
+# --------------------------------------------------------------------------------------------
+def kv_writeback(k_rows, v_rows, offsets, kept_pos, k_blk, v_blk, cap: Optional[int] = None):
+    """The kept tokens' fresh K/V replace the cached block KV at their positions; evicted
+    positions keep their cached values ([PP, "Runtime Action"]: intra-block KV caching; [NEWS,
+    "Arquitetura do FOCUS"]: compacted state).
+
+    k_rows, v_rows: [T, Hkv, d], row n being request r's token kept_pos[n] for
+    offsets[r] <= n < offsets[r+1]; rows n >= cap are absent.  k_blk [B, Hkv, d/8, blk, 8] and
+    v_blk [B, Hkv, blk/8, d, 8] (any dtype: a byte move).  Returns new (k_blk, v_blk).
+    """
+    kb, vb = k_blk.copy(), v_blk.copy()
+    Hkv, d = k_rows.shape[1], k_rows.shape[2]
+    T = int(offsets[-1]) if cap is None else min(int(offsets[-1]), cap)
+    for r in range(len(offsets) - 1):
+        for n in range(int(offsets[r]), min(int(offsets[r + 1]), T)):
+            j = int(kept_pos[n])
+            kb[r, :, :, j, :] = k_rows[n].reshape(Hkv, d // 8, 8)   # key (j, c) at [c//8, j, c%8]
+            vb[r, :, j // 8, :, j % 8] = v_rows[n]                  # value (j, c) at [j//8, c, j%8]
+    return kb, vb
+
+
+def block_commit(commit, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, free_pages,
+                 free_count: int):
+    """Appends each committed request's finished block (all blk tokens) to its paged prefix
+    ([PP, "Motivation"]: finished blocks are exactly KV-cached; [NEWS]: KV-cache management).
+
+    Request r's block token t goes to prefix position P_r + t.  The pages this needs beyond the
+    ceil(P_r / S) it holds are taken from the top of the free-page stack
+    free_pages[0 .. free_count-1], requests in batch order, each request's pages in position
+    order.  Status 0: done.  Status 2: a committed request would outgrow its page table row.
+    Status 1: not enough free pages.  On a non-zero status nothing changes.
+    Returns (k_cache, v_cache, page_table, prefix_len, free_count, status) as new arrays.
+    """
+    S = k_cache.shape[3]
+    blk = k_blk.shape[3]
+    max_pages = page_table.shape[1]
+    kc, vc = k_cache.copy(), v_cache.copy()
+    table, plen = page_table.copy(), np.asarray(prefix_len).copy()
+    B = len(plen)
+    need = np.zeros(B, dtype=np.int64)
+    for r in range(B):
+        if commit[r]:
+            P = int(plen[r])
+            if P + blk > max_pages * S:
+                return k_cache.copy(), v_cache.copy(), page_table.copy(), plen, free_count, 2
+            need[r] = -(-(P + blk) // S) - (-(-P // S))
+    if need.sum() > free_count:
+        return kc, vc, table, plen, free_count, 1
+    top = int(free_count)
+    for r in range(B):
+        if not commit[r]:
+            continue
+        P = int(plen[r])
+        first_new = -(-P // S)
+        for i in range(int(need[r])):
+            top -= 1
+            table[r, first_new + i] = free_pages[top]
+        for t in range(blk):
+            p = P + t
+            page, slot = int(table[r, p // S]), p % S
+            kc[page, :, :, slot, :] = k_blk[r, :, :, t, :]
+            vc[page, :, slot // 8, :, slot % 8] = v_blk[r, :, t // 8, :, t % 8]
+        plen[r] = P + blk
+    return kc, vc, table, plen, top, 0
+
+
+# --------------------------------------------------------------------------------------------
 # the whole step
 # --------------------------------------------------------------------------------------------
 def step(st, hidden: bool = True):

@@ -468,3 +468,114 @@ def test_bf16_decoder_exact():
     assert back[0] == 1.0 and back[1] == -2.5 and back[2] == 45.25
     # 1/3 rounds to the nearest bf16: 0x3EAB = 0.333984375
     assert bits[4] == 0x3EAB and back[4] == 0.333984375
+
+
+# ------------------------------------------------------------------ KV write-back / block commit
+def _logical_block(k_blk, v_blk, r, g):
+    # the block's keys/values of request r, kv head g, read through request_kv's layout reader
+    # (an empty prefix leaves just the block)
+    B, Hkv = k_blk.shape[0], k_blk.shape[1]
+    d = k_blk.shape[2] * 8
+    kc = np.zeros((1, Hkv, d // 8, 16, 8))
+    vc = np.zeros((1, Hkv, 2, d, 8))
+    return O.request_kv(r, g, kc, vc, np.zeros((B, 1), np.int32), np.zeros(B, np.int32),
+                        k_blk, v_blk)
+
+
+def test_kv_writeback_replaces_kept_positions_only():
+    rng = np.random.default_rng(31)
+    B, blk, Hkv, d = 3, 16, 2, 16
+    k_blk = rng.standard_normal((B, Hkv, d // 8, blk, 8))
+    v_blk = rng.standard_normal((B, Hkv, blk // 8, d, 8))
+    keep = np.zeros((B, blk), dtype=np.uint8)
+    keep[0, [1, 7, 15]] = 1
+    keep[2, [0]] = 1
+    offsets, kept_pos, _ = O.compact(keep)
+    T = int(offsets[-1])
+    k_rows = rng.standard_normal((T, Hkv, d))
+    v_rows = rng.standard_normal((T, Hkv, d))
+    kb, vb = O.kv_writeback(k_rows, v_rows, offsets, kept_pos, k_blk, v_blk)
+    for r in range(B):
+        for g in range(Hkv):
+            K0, V0 = _logical_block(k_blk, v_blk, r, g)
+            K1, V1 = _logical_block(kb, vb, r, g)
+            for j in range(blk):
+                n = [m for m in range(offsets[r], offsets[r + 1]) if kept_pos[m] == j]
+                if n:
+                    np.testing.assert_array_equal(K1[j], k_rows[n[0], g])
+                    np.testing.assert_array_equal(V1[j], v_rows[n[0], g])
+                else:
+                    np.testing.assert_array_equal(K1[j], K0[j])
+                    np.testing.assert_array_equal(V1[j], V0[j])
+    # a capacity below T drops the rows at or past it
+    kb2, _ = O.kv_writeback(k_rows, v_rows, offsets, kept_pos, k_blk, v_blk, cap=2)
+    K2, _ = _logical_block(kb2, vb, 0, 0)
+    np.testing.assert_array_equal(K2[15], _logical_block(k_blk, v_blk, 0, 0)[0][15])
+
+
+def _pool(rng, B, Hkv, d, S, plen, spare):
+    npg = [-(-int(P) // S) for P in plen]
+    used = sum(npg)
+    pool = used + spare
+    kc = rng.standard_normal((pool, Hkv, d // 8, S, 8))
+    vc = rng.standard_normal((pool, Hkv, S // 8, d, 8))
+    table = np.full((B, 8), -1, dtype=np.int32)
+    base = 0
+    for r in range(B):
+        table[r, : npg[r]] = np.arange(base, base + npg[r])
+        base += npg[r]
+    free = np.arange(used, pool, dtype=np.int32)
+    return kc, vc, table, free
+
+
+def test_block_commit_appends_block_to_prefix():
+    # after the commit, the request's keys/values read through its page table are the old
+    # prefix followed by the whole block (request_kv is the independent layout reader)
+    rng = np.random.default_rng(32)
+    B, blk, Hkv, d, S = 3, 16, 2, 16, 16
+    plen = np.array([16, 5, 40], dtype=np.int32)
+    kc, vc, table, free = _pool(rng, B, Hkv, d, S, plen, spare=6)
+    k_blk = rng.standard_normal((B, Hkv, d // 8, blk, 8))
+    v_blk = rng.standard_normal((B, Hkv, blk // 8, d, 8))
+    commit = np.array([1, 1, 0], dtype=np.uint8)
+    kc2, vc2, table2, plen2, fc, status = O.block_commit(commit, k_blk, v_blk, kc, vc, table,
+                                                         plen, free, len(free))
+    assert status == 0
+    np.testing.assert_array_equal(plen2, [32, 21, 40])
+    for r in range(B):
+        for g in range(Hkv):
+            Kold, Vold = O.request_kv(r, g, kc, vc, table, plen, k_blk, v_blk)
+            Knew, Vnew = O.request_kv(r, g, kc2, vc2, table2, plen2, k_blk, v_blk)
+            if commit[r]:
+                # [old prefix, block] then the block again (request_kv appends k_blk)
+                np.testing.assert_array_equal(Knew[: plen[r] + blk], Kold)
+                np.testing.assert_array_equal(Vnew[: plen[r] + blk], Vold)
+            else:
+                np.testing.assert_array_equal(Knew, Kold)
+
+
+def test_block_commit_page_allocation_order_and_failures():
+    # S = blk = 16: request 0 (P=16) needs one page, request 1 (P=5 -> 21 tokens) one more,
+    # request 2 is not committed: pages come off the top of the stack in request order
+    rng = np.random.default_rng(33)
+    B, blk, Hkv, d, S = 3, 16, 1, 8, 16
+    plen = np.array([16, 5, 3], dtype=np.int32)
+    kc, vc, table, _ = _pool(rng, B, Hkv, d, S, plen, spare=0)
+    kc = np.concatenate([kc, np.zeros((14,) + kc.shape[1:])])
+    vc = np.concatenate([vc, np.zeros((14,) + vc.shape[1:])])
+    free = np.array([10, 11, 12, 13], dtype=np.int32)
+    k_blk = rng.standard_normal((B, Hkv, d // 8, blk, 8))
+    v_blk = rng.standard_normal((B, Hkv, blk // 8, d, 8))
+    commit = np.array([1, 1, 0], dtype=np.uint8)
+    _, _, t2, p2, fc, st = O.block_commit(commit, k_blk, v_blk, kc, vc, table, plen, free, 4)
+    assert st == 0 and fc == 2
+    assert t2[0, 1] == 13 and t2[1, 1] == 12 and t2[2, 1] == -1
+    # two free pages are not enough for three committed requests needing one each
+    _, _, t3, p3, fc3, st3 = O.block_commit(np.ones(3, np.uint8), k_blk, v_blk, kc, vc, table,
+                                            plen, free, 2)
+    assert st3 == 1 and fc3 == 2 and np.array_equal(t3, table) and np.array_equal(p3, plen)
+    # a request that would outgrow its table row fails the whole commit
+    plen_full = np.array([16, 5, 8 * S - 4], dtype=np.int32)
+    _, _, t4, p4, fc4, st4 = O.block_commit(np.ones(3, np.uint8), k_blk, v_blk, kc, vc, table,
+                                            plen_full, free, 4)
+    assert st4 == 2 and fc4 == 4 and np.array_equal(p4, plen_full)
