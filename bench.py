@@ -256,6 +256,60 @@ def full_domain_pass(inp, t, st, args, stream):
             "layer_lse_attention_us": round(lse_ms * 1000, 2)}
 
 
+def kv_pass(fs, inp, st, args, stream):
+    """Intra-block KV write-back of the kept rows (fresh K/V stand-ins: the gathered Q rows'
+    first Hkv heads) and the commit of every request's block into its paged prefix, each timed
+    by HIP events; the commit runs on a copy of the caches extended by free pages."""
+    import torch
+    from decodability_aware_token_amd import binding as F
+    dev = inp.q_att.device
+    T = int(fs.offsets[-1])
+    rows = fs.q_rows[:, : st.Hkv].contiguous()        # [cap, Hkv, d] bf16
+    kb, vb = inp.k_blk.clone(), inp.v_blk.clone()
+    S = st.S
+    extra = st.B * (-(-st.blk // S) + 1)
+    kc = torch.cat([inp.k_cache, torch.zeros((extra,) + tuple(inp.k_cache.shape[1:]),
+                                             dtype=inp.k_cache.dtype, device=dev)])
+    vc = torch.cat([inp.v_cache, torch.zeros((extra,) + tuple(inp.v_cache.shape[1:]),
+                                             dtype=inp.v_cache.dtype, device=dev)])
+    cols = int((st.prefix_len.max() + st.blk + S - 1) // S)
+    pt = torch.full((st.B, max(cols, inp.page_table.shape[1])), -1, dtype=torch.int32, device=dev)
+    pt[:, : inp.page_table.shape[1]] = inp.page_table
+    free = torch.arange(inp.k_cache.shape[0], inp.k_cache.shape[0] + extra, dtype=torch.int32,
+                        device=dev)
+    commit = torch.ones(st.B, dtype=torch.uint8, device=dev)
+    pl_out = torch.empty_like(inp.prefix_len)
+    fc_in = torch.tensor([extra], dtype=torch.int32, device=dev)
+    fc_out = torch.empty_like(fc_in)
+    status = torch.empty_like(fc_in)
+    wb = lambda: F.kv_writeback(rows, rows, fs.offsets, fs.kept_pos, kb, vb)
+    cm = lambda: F.block_commit(commit, kb, vb, kc, vc, pt, inp.prefix_len, pl_out, free, fc_in,
+                                fc_out, status)
+    for _ in range(args.warmup):
+        wb()
+        cm()
+    torch.cuda.synchronize()
+    assert int(status[0]) == 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        wb()
+    ev[1].record(stream)
+    for _ in range(args.steps):
+        cm()
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    wb_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    cm_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    wb_bytes = 2 * 2 * T * st.Hkv * st.d * 2 + 4 * (T + st.B + 1)
+    cm_bytes = 2 * 2 * st.B * st.blk * st.Hkv * st.d * 2 + 16 * st.B
+    log(f"[bench] kv write-back {wb_ms * 1000:.1f} us ({wb_bytes / (wb_ms * 1e-3) / 1e9:.0f} GB/s)"
+        f"; block commit {cm_ms * 1000:.1f} us ({cm_bytes / (cm_ms * 1e-3) / 1e9:.0f} GB/s)")
+    return {"writeback_us": round(wb_ms * 1000, 2), "writeback_bytes": wb_bytes,
+            "commit_us": round(cm_ms * 1000, 2), "commit_bytes": cm_bytes,
+            "commit_hbm_frac": round(cm_bytes / (cm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +441,7 @@ def main():
     fdom = None
     if not args.no_full_domain:
         fdom = full_domain_pass(inp, t, st, args, stream)
+    kvres = kv_pass(fs, inp, st, args, stream)
 
     res = {
         "metric": "focused block-tokens/s per diffusion step",
@@ -411,6 +466,7 @@ def main():
             "step_launch": mode, "eager_ms_per_step": round(eager_ms, 5),
             "full_block_step": full,
             "full_domain_score": fdom,
+            "kv_cache": kvres,
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -47,6 +47,10 @@ SIGNATURES = {
                                          _c_void_p] + [_c_int] * 7 + [_c_float, _c_void_p,
                                                                       _c_void_p, _c_void_p,
                                                                       _c_size_t, _c_void_p]),
+    "focus_kv_writeback": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p] * 3),
+    "focus_block_commit": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 2 +
+                           [_c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                            _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
 }
 
 
@@ -211,3 +215,30 @@ def ragged_paged_attn(q, offsets, k_cache, v_cache, page_table, prefix_len, k_bl
                                        _ptr(workspace), wsb, _stream(dev))
     _check("focus_ragged_paged_attn", rc)
     return out, lse
+
+
+def kv_writeback(k_rows, v_rows, offsets, kept_pos, k_blk, v_blk):
+    """Scatter the kept rows' K/V [cap, Hkv, d] into k_blk/v_blk in place (see
+    focus_kv_writeback)."""
+    cap, Hkv, d = k_rows.shape
+    B, blk = k_blk.shape[0], k_blk.shape[3]
+    rc = lib().focus_kv_writeback(_ptr(k_rows), _ptr(v_rows), _ptr(offsets), _ptr(kept_pos),
+                                  cap, B, blk, Hkv, d, _ptr(k_blk), _ptr(v_blk),
+                                  _stream(k_rows.device))
+    _check("focus_kv_writeback", rc)
+
+
+def block_commit(commit, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len_in,
+                 prefix_len_out, free_pages, free_count_in, free_count_out, status):
+    """Append committed requests' blocks to their paged prefix (see focus_block_commit); the
+    cache, page table and the *_out / status tensors are updated in place."""
+    B, Hkv = k_blk.shape[0], k_blk.shape[1]
+    d, blk = k_blk.shape[2] * 8, k_blk.shape[3]
+    num_pages, S = k_cache.shape[0], k_cache.shape[3]
+    max_pages = page_table.shape[1]
+    rc = lib().focus_block_commit(_ptr(commit), _ptr(k_blk), _ptr(v_blk), B, blk, Hkv, d, S,
+                                  _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(page_table),
+                                  max_pages, _ptr(prefix_len_in), _ptr(prefix_len_out),
+                                  _ptr(free_pages), free_pages.numel(), _ptr(free_count_in),
+                                  _ptr(free_count_out), _ptr(status), _stream(k_blk.device))
+    _check("focus_block_commit", rc)

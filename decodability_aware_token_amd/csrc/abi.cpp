@@ -213,4 +213,74 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
   return status_of(focus::launch_attn(a, plan, stream));
 }
 
+
+int focus_kv_writeback(const void* k_rows, const void* v_rows, const int32_t* offsets,
+                       const int32_t* kept_pos, int cap, int B, int blk, int Hkv, int d,
+                       void* k_blk, void* v_blk, hipStream_t stream) {
+  if (!k_rows || !v_rows || !offsets || !kept_pos || !k_blk || !v_blk) return FOCUS_ERR_INVALID_ARG;
+  if (cap < 0 || B <= 0 || blk <= 0 || Hkv <= 0 || d <= 0) return FOCUS_ERR_INVALID_ARG;
+  if (!pow2_in(blk, 16, 64) || (d != 64 && d != 128) || Hkv > 64 || B > kMaxB)
+    return FOCUS_ERR_UNSUPPORTED;
+  if (!aligned16(k_rows) || !aligned16(v_rows) || !aligned16(k_blk) || !aligned16(v_blk))
+    return FOCUS_ERR_INVALID_ARG;
+  if (cap == 0) return FOCUS_OK;
+  focus::WritebackArgs a{};
+  a.k_rows = static_cast<const uint16_t*>(k_rows);
+  a.v_rows = static_cast<const uint16_t*>(v_rows);
+  a.offsets = offsets;
+  a.kept_pos = kept_pos;
+  a.cap = cap;
+  a.B = B;
+  a.blk = blk;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.k_blk = static_cast<uint16_t*>(k_blk);
+  a.v_blk = static_cast<uint16_t*>(v_blk);
+  return status_of(focus::launch_writeback(a, stream));
+}
+
+int focus_block_commit(const uint8_t* commit, const void* k_blk, const void* v_blk, int B,
+                       int blk, int Hkv, int d, int S, void* k_cache, void* v_cache,
+                       int num_pages, int32_t* page_table, int max_pages,
+                       const int32_t* prefix_len_in, int32_t* prefix_len_out,
+                       const int32_t* free_pages, int free_cap, const int32_t* free_count_in,
+                       int32_t* free_count_out, int32_t* status, hipStream_t stream) {
+  if (!commit || !k_blk || !v_blk || !k_cache || !v_cache || !page_table || !prefix_len_in ||
+      !prefix_len_out || !free_count_in || !free_count_out || !status)
+    return FOCUS_ERR_INVALID_ARG;
+  if (free_cap > 0 && !free_pages) return FOCUS_ERR_INVALID_ARG;
+  if (B <= 0 || blk <= 0 || Hkv <= 0 || d <= 0 || S <= 0 || num_pages <= 0 || max_pages <= 0 ||
+      free_cap < 0)
+    return FOCUS_ERR_INVALID_ARG;
+  if (prefix_len_in == prefix_len_out || free_count_in == free_count_out)
+    return FOCUS_ERR_INVALID_ARG;
+  if (!pow2_in(blk, 16, 64) || !pow2_in(S, 16, 64) || (d != 64 && d != 128) || Hkv > 64 ||
+      B > kMaxB || (long long)max_pages * S > (1LL << 24))
+    return FOCUS_ERR_UNSUPPORTED;
+  if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
+    return FOCUS_ERR_INVALID_ARG;
+  focus::CommitArgs a{};
+  a.commit = commit;
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.B = B;
+  a.blk = blk;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.S = S;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.num_pages = num_pages;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.prefix_len_in = prefix_len_in;
+  a.prefix_len_out = prefix_len_out;
+  a.free_pages = free_pages;
+  a.free_cap = free_cap;
+  a.free_count_in = free_count_in;
+  a.free_count_out = free_count_out;
+  a.status = status;
+  return status_of(focus::launch_commit(a, stream));
+}
+
 }  // extern "C"

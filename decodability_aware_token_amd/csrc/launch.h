@@ -85,4 +85,35 @@ struct AttnPlan {
 AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
 
+struct WritebackArgs {
+  const uint16_t* k_rows;  // [cap, Hkv, d]
+  const uint16_t* v_rows;  // [cap, Hkv, d]
+  const int32_t* offsets;  // [B+1]
+  const int32_t* kept_pos; // [cap]
+  int cap, B, blk, Hkv, d;
+  uint16_t* k_blk;         // [B, Hkv, d/8, blk, 8]
+  uint16_t* v_blk;         // [B, Hkv, blk/8, d, 8]
+};
+hipError_t launch_writeback(const WritebackArgs& a, hipStream_t s);
+
+struct CommitArgs {
+  const uint8_t* commit;   // [B]
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  int B, blk, Hkv, d, S;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int num_pages;
+  int32_t* page_table;     // [B, max_pages]
+  int max_pages;
+  const int32_t* prefix_len_in;
+  int32_t* prefix_len_out;
+  const int32_t* free_pages;  // [free_cap]
+  int free_cap;
+  const int32_t* free_count_in;
+  int32_t* free_count_out;
+  int32_t* status;
+};
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+
 }  // namespace focus

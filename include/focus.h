@@ -181,6 +181,56 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
                             int max_kept, float sm_scale, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* --------------------------------------------------------------------------------------------
+ * 5. Intra-block KV write-back.
+ *
+ * Project page, card "Runtime Action" (intra-block KV caching): the layer's fresh K/V of the kept
+ * tokens replace the cached block KV at their positions; evicted positions keep their cached
+ * values.  Row n (offsets[r] <= n < offsets[r+1], n < cap) is request r's token kept_pos[n]:
+ *   k_blk[r, g, c/8, kept_pos[n], c%8] = k_rows[n, g, c]
+ *   v_blk[r, g, kept_pos[n]/8, c, kept_pos[n]%8] = v_rows[n, g, c]
+ *
+ *   k_rows, v_rows  [cap, Hkv, d] bf16 (compacted order, e.g. from the gathered hidden rows)
+ *   offsets [B+1], kept_pos [cap] i32 (as produced by focus_compact)
+ *   k_blk [B, Hkv, d/8, blk, 8], v_blk [B, Hkv, blk/8, d, 8] bf16, updated in place
+ * A row whose kept_pos is outside [0, blk) is skipped; at most blk rows of a request are read.
+ * Supported: blk in {16,32,64}; d in {64,128}; Hkv <= 64; 1 <= B <= 4096; K/V pointers 16-byte
+ * aligned.  cap == 0 does nothing.
+ * ------------------------------------------------------------------------------------------ */
+int focus_kv_writeback(const void* k_rows, const void* v_rows, const int32_t* offsets,
+                       const int32_t* kept_pos, int cap, int B, int blk, int Hkv, int d,
+                       void* k_blk, void* v_blk, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
+ * 6. Block commit: append finished blocks to the paged prefix.
+ *
+ * Project page, card "Motivation" (earlier blocks are exactly KV-cached); AI Engineering Academy
+ * article, "Arquitetura do FOCUS" (KV-cache management).  For every request with commit[r] != 0
+ * its whole block (blk tokens of k_blk/v_blk) becomes prefix positions P_r .. P_r+blk-1, with
+ * P_r = prefix_len_in[r]: token t goes to page page_table[r, (P_r+t)/S], slot (P_r+t)%S.  The
+ * ceil((P_r+blk)/S) - ceil(P_r/S) pages it needs beyond those it holds are popped from the top
+ * of the free-page stack free_pages[0 .. free_count_in-1]: requests in batch order, each
+ * request's pages in position order, written into page_table.  prefix_len_out[r] = P_r + blk
+ * for committed requests, P_r otherwise; free_count_out = free_count_in - pages taken.
+ *   status[0] = 0 done; 1 not enough free pages; 2 a committed request's prefix length is
+ *   negative or P_r + blk exceeds max_pages*S; 3 invalid page data (free_count_in outside
+ *   [0, free_cap], or a page id to be written outside [0, num_pages)).  On status != 0 nothing
+ *   is written except status, prefix_len_out (= prefix_len_in) and free_count_out (= in).
+ *
+ *   commit [B] u8; k_blk, v_blk as in call 4; k_cache, v_cache, page_table updated in place
+ *   prefix_len_in/out [B] i32, free_count_in/out [1] i32, status [1] i32: device memory; the
+ *   in and out arrays must be distinct (every workgroup reads all inputs)
+ *   free_pages [free_cap] i32 (device), free_cap its length
+ * Supported: blk, S in {16,32,64}; d in {64,128}; Hkv <= 64; 1 <= B <= 4096;
+ * max_pages*S <= 2^24; K/V pointers 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+int focus_block_commit(const uint8_t* commit, const void* k_blk, const void* v_blk, int B,
+                       int blk, int Hkv, int d, int S, void* k_cache, void* v_cache,
+                       int num_pages, int32_t* page_table, int max_pages,
+                       const int32_t* prefix_len_in, int32_t* prefix_len_out,
+                       const int32_t* free_pages, int free_cap, const int32_t* free_count_in,
+                       int32_t* free_count_out, int32_t* status, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -173,3 +173,37 @@ def test_attn_plan_is_bounded():
     # the workspace holds per-item counters plus partials sized by the grid, not by the prefixes
     assert F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 8, 4) == \
         F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 64, 4)
+
+
+def test_kv_writeback_errors():
+    def wb(**kw):
+        a = dict(kr=P, vr=P, off=P, pos=P, cap=8, B=4, blk=32, Hkv=8, d=128, kb=P, vb=P)
+        a.update(kw)
+        return F.lib().focus_kv_writeback(a["kr"], a["vr"], a["off"], a["pos"], a["cap"], a["B"],
+                                          a["blk"], a["Hkv"], a["d"], a["kb"], a["vb"], None)
+    assert wb(kr=None) == F.FOCUS_ERR_INVALID_ARG
+    assert wb(pos=None) == F.FOCUS_ERR_INVALID_ARG
+    assert wb(cap=-1) == F.FOCUS_ERR_INVALID_ARG
+    assert wb(blk=48) == F.FOCUS_ERR_UNSUPPORTED
+    assert wb(d=32) == F.FOCUS_ERR_UNSUPPORTED
+    assert wb(kb=P + 4) == F.FOCUS_ERR_INVALID_ARG
+    assert wb(cap=0) == F.FOCUS_OK          # nothing to write, nothing launched
+
+
+def test_block_commit_errors():
+    def bc(**kw):
+        a = dict(cm=P, kb=P, vb=P, B=4, blk=32, Hkv=8, d=128, S=64, kc=P, vc=P, np=100, pt=P,
+                 mp=8, pi=P, po=P + 64, fp=P, fcap=10, fi=P + 128, fo=P + 192, st=P + 256)
+        a.update(kw)
+        return F.lib().focus_block_commit(a["cm"], a["kb"], a["vb"], a["B"], a["blk"], a["Hkv"],
+                                          a["d"], a["S"], a["kc"], a["vc"], a["np"], a["pt"],
+                                          a["mp"], a["pi"], a["po"], a["fp"], a["fcap"], a["fi"],
+                                          a["fo"], a["st"], None)
+    assert bc(cm=None) == F.FOCUS_ERR_INVALID_ARG
+    assert bc(st=None) == F.FOCUS_ERR_INVALID_ARG
+    assert bc(po=P) == F.FOCUS_ERR_INVALID_ARG       # prefix_len in and out alias
+    assert bc(fo=P + 128) == F.FOCUS_ERR_INVALID_ARG # free_count in and out alias
+    assert bc(fp=None) == F.FOCUS_ERR_INVALID_ARG    # pages listed but no array
+    assert bc(S=48) == F.FOCUS_ERR_UNSUPPORTED
+    assert bc(mp=1 << 20) == F.FOCUS_ERR_UNSUPPORTED # max_pages * S > 2^24
+    assert bc(kc=P + 8) == F.FOCUS_ERR_INVALID_ARG

@@ -446,3 +446,119 @@ def test_full_domain_score(name):
     err2 = np.abs(got2.cpu().numpy() - ref).max()
     assert err2 <= DELTA_TOL, err2
     print(f"delta err {err:.2e} (own LSE), {err2:.2e} (oracle LSE)")
+
+
+# ------------------------------------------------------------------ KV write-back / commit
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name,over", [("sdar_b32_blk32", {"B": 6}),
+                                       ("sweep_b128_blk64", {"B": 4, "d": 64}),
+                                       ("sweep_b128_blk16", {"B": 5})])
+def test_kv_writeback(name, over):
+    from workloads import f32_to_bf16_bits
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"kv writeback {name} {over}")
+    rng = np.random.default_rng(41)
+    keep = _random_keep(rng, st.B, st.blk, st.blk // 2)
+    offsets, kept_pos, _ = O.compact(keep)
+    T = int(offsets[-1])
+    k_rows = f32_to_bf16_bits(rng.standard_normal((T, st.Hkv, st.d)).astype(np.float32))
+    v_rows = f32_to_bf16_bits(rng.standard_normal((T, st.Hkv, st.d)).astype(np.float32))
+    ref_k, ref_v = O.kv_writeback(k_rows, v_rows, offsets, kept_pos, st.k_blk, st.v_blk)
+    kb, vb = bf16_tensor(st.k_blk, DEV), bf16_tensor(st.v_blk, DEV)
+    F.kv_writeback(bf16_tensor(k_rows, DEV), bf16_tensor(v_rows, DEV),
+                   torch.from_numpy(offsets).to(DEV), torch.from_numpy(kept_pos).to(DEV), kb, vb)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(kb), ref_k) and np.array_equal(_bits(vb), ref_v)
+
+
+def _commit_case(st, rng, nfree, commit, shuffle=True):
+    """Device state for a commit: the step's caches plus nfree free pages (the stack)."""
+    pool = st.k_cache.shape[0]
+    kc = np.concatenate([st.k_cache, np.zeros((nfree,) + st.k_cache.shape[1:], np.uint16)])
+    vc = np.concatenate([st.v_cache, np.zeros((nfree,) + st.v_cache.shape[1:], np.uint16)])
+    free = np.arange(pool, pool + nfree, dtype=np.int32)
+    if shuffle:
+        free = rng.permutation(free).astype(np.int32)
+    return kc, vc, free
+
+
+def _run_commit(st, kc, vc, table, plen, free, fc, commit):
+    d = {"kc": bf16_tensor(kc, DEV), "vc": bf16_tensor(vc, DEV),
+         "pt": torch.from_numpy(table.copy()).to(DEV),
+         "pi": torch.from_numpy(plen.copy()).to(DEV),
+         "po": torch.full((st.B,), -7, dtype=torch.int32, device=DEV),
+         "fp": torch.from_numpy(free).to(DEV),
+         "fi": torch.tensor([fc], dtype=torch.int32, device=DEV),
+         "fo": torch.full((1,), -7, dtype=torch.int32, device=DEV),
+         "st": torch.full((1,), -7, dtype=torch.int32, device=DEV)}
+    F.block_commit(torch.from_numpy(commit).to(DEV), bf16_tensor(st.k_blk, DEV),
+                   bf16_tensor(st.v_blk, DEV), d["kc"], d["vc"], d["pt"], d["pi"], d["po"],
+                   d["fp"], d["fi"], d["fo"], d["st"])
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("name,over", [("sdar_b32_blk32", {"B": 6}),
+                                       ("longctx_b64_blk32", {"B": 3}),
+                                       ("sweep_b128_blk16", {"B": 4, "S": 32}),
+                                       ("tiny_b2_blk16", {"B": 5, "prefix": ("uniform", 0, 40),
+                                                          "score_dtype": "bf16"})])
+def test_block_commit(name, over):
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"block commit {name} {over} plen={st.prefix_len.tolist()}")
+    rng = np.random.default_rng(43)
+    commit = (rng.random(st.B) < 0.7).astype(np.uint8)
+    commit[0] = 1
+    nfree = int(np.ceil(st.blk / st.S) + 1) * st.B + 3
+    # the table rows must have room for one more block
+    table = st.page_table
+    need_cols = int((st.prefix_len.max() + st.blk + st.S - 1) // st.S)
+    if table.shape[1] < need_cols:
+        table = np.concatenate([table, np.full((st.B, need_cols - table.shape[1]), -1,
+                                               np.int32)], axis=1)
+    kc, vc, free = _commit_case(st, rng, nfree, commit)
+    ref = O.block_commit(commit, st.k_blk, st.v_blk, kc, vc, table, st.prefix_len, free, nfree)
+    d = _run_commit(st, kc, vc, table, st.prefix_len, free, nfree, commit)
+    assert int(d["st"][0]) == ref[5] == 0
+    assert int(d["fo"][0]) == ref[4]
+    assert np.array_equal(d["po"].cpu().numpy(), ref[3])
+    assert np.array_equal(d["pt"].cpu().numpy(), ref[2])
+    assert np.array_equal(_bits(d["kc"]), ref[0]) and np.array_equal(_bits(d["vc"]), ref[1])
+    # the committed state is attended like any prefix: the attention over it equals the
+    # oracle's over the oracle's committed state
+    keep = _random_keep(rng, st.B, st.blk, 4, empty_frac=0.0)
+    c = attn_case_inputs(st, keep)
+    o_out, o_lse = O.ragged_paged_attn(c["q_rows64"], c["offsets"], O.bf16_to_f64(ref[0]),
+                                       O.bf16_to_f64(ref[1]), ref[2], ref[3],
+                                       O.bf16_to_f64(st.k_blk), O.bf16_to_f64(st.v_blk),
+                                       st.sm_scale)
+    out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], d["kc"], d["vc"], d["pt"], d["po"],
+                                   bf16_tensor(st.k_blk, DEV), bf16_tensor(st.v_blk, DEV), 4,
+                                   st.sm_scale)
+    torch.cuda.synchronize()
+    T = int(c["offsets"][-1])
+    assert np.abs(out[:T].float().cpu().numpy() - o_out).max() <= OUT_TOL
+    assert np.abs(lse[:T].cpu().numpy() - o_lse).max() <= LSE_TOL
+
+
+def test_block_commit_failures_change_nothing():
+    st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=4))
+    _announce("block commit failures")
+    rng = np.random.default_rng(44)
+    commit = np.ones(st.B, np.uint8)
+    table = np.concatenate([st.page_table, np.full((st.B, 2), -1, np.int32)], axis=1)
+    kc, vc, free = _commit_case(st, rng, 2, commit)
+    aligned = (st.S * np.arange(1, st.B + 1)).astype(np.int32)   # one new page each
+    for plen, fc, want in ((aligned, 2, 1),                                        # out of pages
+                           (np.where(np.arange(st.B) == 2, table.shape[1] * st.S - 3,
+                                     st.prefix_len).astype(np.int32), 2, 2),       # row overflow
+                           (st.prefix_len, 5, 3)):                                 # count > stack
+        d = _run_commit(st, kc, vc, table, plen, free, fc, commit)
+        assert int(d["st"][0]) == want
+        assert int(d["fo"][0]) == fc
+        assert np.array_equal(d["po"].cpu().numpy(), plen)
+        assert np.array_equal(d["pt"].cpu().numpy(), table)
+        assert np.array_equal(_bits(d["kc"]), kc) and np.array_equal(_bits(d["vc"]), vc)
