@@ -47,6 +47,14 @@ SIGNATURES = {
                                          _c_void_p] + [_c_int] * 7 + [_c_float, _c_void_p,
                                                                       _c_void_p, _c_void_p,
                                                                       _c_size_t, _c_void_p]),
+    "focus_score_select": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_void_p,
+                                                                  _c_void_p, _c_int, _c_float,
+                                                                  _c_int, _c_int, _c_void_p,
+                                                                  _c_void_p, _c_void_p,
+                                                                  _c_void_p, _c_size_t,
+                                                                  _c_void_p]),
+    "focus_compact_multi": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "focus_kv_writeback": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p] * 3),
     "focus_block_commit": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 2 +
                            [_c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -242,3 +250,52 @@ def block_commit(commit, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len_
                                   _ptr(free_pages), free_pages.numel(), _ptr(free_count_in),
                                   _ptr(free_count_out), _ptr(status), _stream(k_blk.device))
     _check("focus_block_commit", rc)
+
+
+def score_select(q0, k0, q1, k1, sm_scale: float, masked, budget=None, adaptive=None, delta=None,
+                 keep=None, kept_count=None, workspace=None):
+    """delta, keep, kept_count of focus_score_l01 followed by focus_select_budget, in one launch
+    (see focus_score_select)."""
+    B, blk, Hq, d = q0.shape
+    Hkv = k0.shape[2]
+    dev = q0.device
+    dt = {torch.float32: FOCUS_F32, torch.bfloat16: FOCUS_BF16}[q0.dtype]
+    if delta is None:
+        delta = torch.empty((B, blk), dtype=torch.float32, device=dev)
+    if keep is None:
+        keep = torch.empty((B, blk), dtype=torch.uint8, device=dev)
+    if kept_count is None:
+        kept_count = torch.empty(B, dtype=torch.int32, device=dev)
+    ad, beta, lo, hi = (0, 0.0, 0, 0) if adaptive is None else (1,) + tuple(adaptive)
+    need = lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
+    workspace, wsb = _workspace(need, dev, workspace)
+    rc = lib().focus_score_select(_ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), dt, B, blk, Hq, Hkv, d,
+                                  float(sm_scale), _ptr(masked), _ptr(budget), ad, float(beta),
+                                  int(lo), int(hi), _ptr(delta), _ptr(keep), _ptr(kept_count),
+                                  _ptr(workspace), wsb, _stream(dev))
+    _check("focus_score_select", rc)
+    return delta, keep, kept_count
+
+
+def compact_multi(keep, row_sets, cap: int, offsets=None, kept_pos=None, gathered=None):
+    """offsets, kept_pos and one gathered tensor per row set [B, blk, ...] (see
+    focus_compact_multi); ``gathered`` optionally gives the output tensors."""
+    B, blk = keep.shape
+    dev = keep.device
+    n = len(row_sets)
+    if offsets is None:
+        offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if kept_pos is None:
+        kept_pos = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if gathered is None:
+        gathered = [torch.empty((max(cap, 1),) + tuple(r.shape[2:]), dtype=r.dtype, device=dev)
+                    for r in row_sets]
+    if not all(t.is_contiguous() for t in list(row_sets) + list(gathered)):
+        raise ValueError("tensors handed to libfocus must be contiguous")
+    rows_arr = (_c_void_p * max(n, 1))(*[r.data_ptr() for r in row_sets])
+    bytes_arr = (_c_int64 * max(n, 1))(*[r[0, 0].numel() * r.element_size() for r in row_sets])
+    out_arr = (_c_void_p * max(n, 1))(*[g.data_ptr() for g in gathered])
+    rc = lib().focus_compact_multi(_ptr(keep), B, blk, n, rows_arr, bytes_arr, out_arr, int(cap),
+                                   _ptr(offsets), _ptr(kept_pos), _stream(dev))
+    _check("focus_compact_multi", rc)
+    return offsets, kept_pos, gathered

@@ -53,7 +53,8 @@ namespace {
 int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
                  const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
                  int Hkv, int d, float sm_scale, float* delta, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 size_t workspace_bytes, hipStream_t stream,
+                 const focus::SelectArgs* sel = nullptr) {
   if (!q0 || !k0 || !q1 || !k1 || !delta) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FOCUS_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return FOCUS_ERR_INVALID_ARG;
@@ -81,9 +82,11 @@ int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
   a.lse0 = lse0;
   a.lse1 = lse1;
   a.delta = delta;
-  a.counters = static_cast<int*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                    focus::score_counter_bytes(B));
+  a.part = static_cast<float*>(workspace);
+  if (sel) {
+    a.fuse_select = 1;
+    a.sel = *sel;
+  }
   return status_of(focus::launch_score(a, stream));
 }
 }  // namespace
@@ -102,6 +105,30 @@ int focus_score_l01_lse(const void* q0, const void* k0, const void* q1, const vo
   if (!lse0 || !lse1) return FOCUS_ERR_INVALID_ARG;
   return score_common(q0, k0, q1, k1, lse0, lse1, dtype, B, blk, Hq, Hkv, d, sm_scale, delta,
                       workspace, workspace_bytes, stream);
+}
+
+int focus_score_select(const void* q0, const void* k0, const void* q1, const void* k1,
+                       int dtype, int B, int blk, int Hq, int Hkv, int d, float sm_scale,
+                       const uint8_t* masked, const int32_t* budget, int adaptive, float beta,
+                       int lo, int hi, float* delta, uint8_t* keep, int32_t* kept_count,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!masked || !keep || !kept_count) return FOCUS_ERR_INVALID_ARG;
+  if (!adaptive && !budget) return FOCUS_ERR_INVALID_ARG;
+  if (adaptive && (!std::isfinite(beta) || lo > hi)) return FOCUS_ERR_INVALID_ARG;
+  focus::SelectArgs sa{};
+  sa.delta = delta;
+  sa.masked = masked;
+  sa.budget = budget;
+  sa.adaptive = adaptive ? 1 : 0;
+  sa.beta = beta;
+  sa.lo = lo;
+  sa.hi = hi;
+  sa.B = B;
+  sa.blk = blk;
+  sa.keep = keep;
+  sa.kept_count = kept_count;
+  return score_common(q0, k0, q1, k1, nullptr, nullptr, dtype, B, blk, Hq, Hkv, d, sm_scale,
+                      delta, workspace, workspace_bytes, stream, &sa);
 }
 
 int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t* budget,
@@ -127,31 +154,50 @@ int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t
   return status_of(focus::launch_select(a, stream));
 }
 
-int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
-                  int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,
-                  hipStream_t stream) {
+namespace {
+int compact_common(const uint8_t* keep, int B, int blk, int nsets, const void* const* rows,
+                   const int64_t* row_bytes, void* const* gathered, int cap, int32_t* offsets,
+                   int32_t* kept_pos, hipStream_t stream) {
   if (!keep || !offsets) return FOCUS_ERR_INVALID_ARG;
-  if (B <= 0 || blk <= 0 || cap < 0) return FOCUS_ERR_INVALID_ARG;
-  if ((rows == nullptr) != (gathered == nullptr)) return FOCUS_ERR_INVALID_ARG;
+  if (B <= 0 || blk <= 0 || cap < 0 || nsets < 0) return FOCUS_ERR_INVALID_ARG;
+  if (nsets > 0 && (!rows || !row_bytes || !gathered)) return FOCUS_ERR_INVALID_ARG;
   if (!aligned4(keep)) return FOCUS_ERR_INVALID_ARG;
-  if (!pow2_in(blk, 16, 64) || B > kMaxB) return FOCUS_ERR_UNSUPPORTED;
-  if (rows) {
-    if (row_bytes <= 0) return FOCUS_ERR_INVALID_ARG;
-    if (row_bytes % 16 != 0 || row_bytes > kMaxRowBytes || !aligned16(rows) ||
-        !aligned16(gathered))
-      return FOCUS_ERR_UNSUPPORTED;
-  }
+  if (!pow2_in(blk, 16, 64) || B > kMaxB || nsets > focus::kMaxSets) return FOCUS_ERR_UNSUPPORTED;
   focus::CompactArgs a{};
+  for (int si = 0; si < nsets; ++si) {
+    if (!rows[si] || !gathered[si] || row_bytes[si] <= 0) return FOCUS_ERR_INVALID_ARG;
+    if (row_bytes[si] % 16 != 0 || row_bytes[si] > kMaxRowBytes || !aligned16(rows[si]) ||
+        !aligned16(gathered[si]))
+      return FOCUS_ERR_UNSUPPORTED;
+    a.rows[si] = rows[si];
+    a.row_bytes[si] = row_bytes[si];
+    a.gathered[si] = gathered[si];
+  }
   a.keep = keep;
   a.B = B;
   a.blk = blk;
-  a.rows = rows;
-  a.row_bytes = rows ? row_bytes : 0;
+  a.nsets = nsets;
   a.cap = cap;
   a.offsets = offsets;
   a.kept_pos = kept_pos;
-  a.gathered = gathered;
   return status_of(focus::launch_compact(a, stream));
+}
+}  // namespace
+
+int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
+                  int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,
+                  hipStream_t stream) {
+  if ((rows == nullptr) != (gathered == nullptr)) return FOCUS_ERR_INVALID_ARG;
+  if (rows && row_bytes <= 0) return FOCUS_ERR_INVALID_ARG;
+  return compact_common(keep, B, blk, rows ? 1 : 0, &rows, &row_bytes, &gathered, cap, offsets,
+                        kept_pos, stream);
+}
+
+int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const void* const* rows,
+                        const int64_t* row_bytes, void* const* gathered, int cap,
+                        int32_t* offsets, int32_t* kept_pos, hipStream_t stream) {
+  return compact_common(keep, B, blk, nsets, rows, row_bytes, gathered, cap, offsets, kept_pos,
+                        stream);
 }
 
 size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, int d, int S,

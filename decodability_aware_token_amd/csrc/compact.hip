@@ -77,23 +77,28 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   __syncthreads();
   const int k_all = s_k;
 
-  // 3. first gather batch: loads only
-  const bool gather = a.gathered != nullptr && k_all > 0;
-  const int chunks = gather ? (int)(a.row_bytes / 16) : 0;  // row_bytes <= 2^24
-  const int total = k_all * chunks;
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rows);
-  unsigned char* dst = reinterpret_cast<unsigned char*>(a.gathered);
-  auto src_of = [&](int c) {
-    const int t = c / chunks, cc = c - t * chunks;
-    return src + ((int64_t)r * blk + s_pos[t]) * a.row_bytes + (int64_t)cc * 16;
-  };
-  // unconditional (a request with nothing to gather reads 16 bytes of its own keep row), so
-  // that no join makes the compiler wait for these loads before the count below
+  // 3. first gather batch of each row set: loads only.  Unconditional (a request with nothing
+  // to gather reads 16 bytes of its own keep row), so that no join makes the compiler wait for
+  // these loads before the count below.
   const unsigned char* dummy = a.keep + (size_t)r * blk;
-  uint4 v[kGatherBatch];
+  const bool gather = a.nsets > 0 && k_all > 0;
+  int chunks[kMaxSets], total[kMaxSets];
 #pragma unroll
-  for (int u = 0; u < kGatherBatch; ++u)
-    v[u] = load16(total > 0 ? src_of(min(tid + u * 256, total - 1)) : dummy);
+  for (int si = 0; si < kMaxSets; ++si) {
+    chunks[si] = (gather && si < a.nsets) ? (int)(a.row_bytes[si] / 16) : 0;  // <= 2^20
+    total[si] = k_all * chunks[si];
+  }
+  auto src_of = [&](int si, int c) {
+    const int t = c / chunks[si], cc = c - t * chunks[si];
+    return static_cast<const unsigned char*>(a.rows[si]) +
+           ((int64_t)r * blk + s_pos[t]) * a.row_bytes[si] + (int64_t)cc * 16;
+  };
+  uint4 v[kMaxSets][kGatherBatch];
+#pragma unroll
+  for (int si = 0; si < kMaxSets; ++si)
+#pragma unroll
+    for (int u = 0; u < kGatherBatch; ++u)
+      v[si][u] = load16(total[si] > 0 ? src_of(si, min(tid + u * 256, total[si] - 1)) : dummy);
 
   // 4. base = kept tokens of the predecessors
   int cnt = 0;
@@ -116,23 +121,30 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   if (!gather) return;
   const int k = min(k_all, a.cap - base);  // rows at or past cap are not written
   if (k <= 0) return;
-  const int limit = k * chunks;
-  auto dst_of = [&](int c) {
-    const int t = c / chunks, cc = c - t * chunks;
-    return dst + ((int64_t)base + t) * a.row_bytes + (int64_t)cc * 16;
-  };
 #pragma unroll
-  for (int u = 0; u < kGatherBatch; ++u) {
-    const int c = tid + u * 256;
-    if (c < limit) *reinterpret_cast<uint4*>(dst_of(c)) = v[u];
-  }
-  for (int c0 = tid + 256 * kGatherBatch; c0 < limit; c0 += 256 * kGatherBatch) {
-#pragma unroll
-    for (int u = 0; u < kGatherBatch; ++u) v[u] = load16(src_of(min(c0 + u * 256, limit - 1)));
+  for (int si = 0; si < kMaxSets; ++si) {
+    if (si >= a.nsets) break;
+    const int limit = k * chunks[si];
+    unsigned char* dst = static_cast<unsigned char*>(a.gathered[si]);
+    auto dst_of = [&](int c) {
+      const int t = c / chunks[si], cc = c - t * chunks[si];
+      return dst + ((int64_t)base + t) * a.row_bytes[si] + (int64_t)cc * 16;
+    };
 #pragma unroll
     for (int u = 0; u < kGatherBatch; ++u) {
-      const int c = c0 + u * 256;
-      if (c < limit) *reinterpret_cast<uint4*>(dst_of(c)) = v[u];
+      const int c = tid + u * 256;
+      if (c < limit) *reinterpret_cast<uint4*>(dst_of(c)) = v[si][u];
+    }
+    for (int c0 = tid + 256 * kGatherBatch; c0 < limit; c0 += 256 * kGatherBatch) {
+      uint4 w[kGatherBatch];
+#pragma unroll
+      for (int u = 0; u < kGatherBatch; ++u)
+        w[u] = load16(src_of(si, min(c0 + u * 256, limit - 1)));
+#pragma unroll
+      for (int u = 0; u < kGatherBatch; ++u) {
+        const int c = c0 + u * 256;
+        if (c < limit) *reinterpret_cast<uint4*>(dst_of(c)) = w[u];
+      }
     }
   }
 }

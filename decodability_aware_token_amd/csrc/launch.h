@@ -8,24 +8,6 @@
 
 namespace focus {
 
-struct ScoreArgs {
-  const void* q0;
-  const void* k0;
-  const void* q1;
-  const void* k1;
-  int is_bf16;
-  int B, blk, Hq, Hkv, d;
-  float scale_log2;  // sm_scale * log2(e)
-  const float* lse0; // [B, blk, Hq] full-domain row log-sum-exp of layer 0, or null (block-only)
-  const float* lse1; // same for layer 1
-  float* delta;      // [B, blk]
-  int* counters;     // workspace [B] arrival counters (zero between calls)
-  float* part;       // workspace [B, Hkv, blk]
-};
-inline size_t score_counter_bytes(int B) { return ((size_t)B * sizeof(int) + 255) & ~(size_t)255; }
-size_t score_workspace_bytes(int B, int blk, int Hkv);
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
-
 struct SelectArgs {
   const float* delta;
   const uint8_t* masked;
@@ -37,17 +19,37 @@ struct SelectArgs {
   uint8_t* keep;
   int32_t* kept_count;
 };
+struct ScoreArgs {
+  const void* q0;
+  const void* k0;
+  const void* q1;
+  const void* k1;
+  int is_bf16;
+  int B, blk, Hq, Hkv, d;
+  float scale_log2;  // sm_scale * log2(e)
+  const float* lse0; // [B, blk, Hq] full-domain row log-sum-exp of layer 0, or null (block-only)
+  const float* lse1; // same for layer 1
+  float* delta;      // [B, blk]
+  float* part;       // workspace [B, Hkv, blk]
+  int fuse_select;   // run the selection of each request right after its delta
+  SelectArgs sel;    // (delta unused: the request's delta is in registers)
+};
+size_t score_workspace_bytes(int B, int blk, int Hkv);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
+constexpr int kMaxSets = 2;  // row sets gathered by one compaction launch
 struct CompactArgs {
   const uint8_t* keep;
   int B, blk;
-  const void* rows;
-  int64_t row_bytes;
+  int nsets;                      // 0 (offsets and positions only) .. kMaxSets
+  const void* rows[kMaxSets];     // [B, blk, row_bytes[s]]
+  int64_t row_bytes[kMaxSets];
+  void* gathered[kMaxSets];       // [cap, row_bytes[s]]
   int cap;
   int32_t* offsets;
   int32_t* kept_pos;
-  void* gathered;
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 

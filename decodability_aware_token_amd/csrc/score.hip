@@ -10,10 +10,11 @@
 // of each 16-key tile: the row softmax over keys needs a local reduction plus two cross-lane
 // steps, and the column sums accumulate in registers across units and both layers (layer 0
 // subtracts, layer 1 adds).  The 16 query lanes are summed once at the end, the 4 waves in LDS
-// in a fixed order; the last of a request's Hkv workgroups to finish sums their partials in
-// kv-head order (an arrival counter per request), so the result is deterministic.
+// in a fixed order.  A second small kernel sums each request's Hkv partials in kv-head order
+// (deterministic, no atomics) and can run the request's selection right away.
 #include "device_common.h"
 #include "launch.h"
+#include "select_impl.h"
 
 namespace focus {
 namespace {
@@ -158,9 +159,7 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
                                                             int Hkv, float scale_log2,
                                                             const float* __restrict__ lse0,
                                                             const float* __restrict__ lse1,
-                                                            float* __restrict__ part,
-                                                            int* __restrict__ counters,
-                                                            float* __restrict__ delta) {
+                                                            float* __restrict__ part) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int ROW = D + 16 / sizeof(T);
   constexpr int NMT = BLK / 16;
@@ -219,30 +218,27 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
       if (n16 == 0) red[wave * BLK + 16 * mt + 4 * j4 + i] = v;
     }
   __syncthreads();
-  // The Hkv workgroups of request r meet through an arrival counter: each stores its partial
-  // with device-scope stores (coherent across the XCDs' L2s), waits for them, and arrives; the
-  // last one sums the Hkv partials in kv-head order and resets the counter for the next call.
-  __shared__ int s_last;
-  if (tid < BLK) {
-    const float v = ((red[tid] + red[BLK + tid]) + red[2 * BLK + tid]) + red[3 * BLK + tid];
-    __hip_atomic_store(part + (size_t)blockIdx.x * BLK + tid, v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < BLK)
+    part[(size_t)blockIdx.x * BLK + tid] =
+        ((red[tid] + red[BLK + tid]) + red[2 * BLK + tid]) + red[3 * BLK + tid];
+}
+
+// One wave per request: lane j sums the Hkv partials of position j in kv-head order (fixed
+// order: deterministic), writes delta, and optionally runs the request's selection on it.
+__global__ __launch_bounds__(256) void score_reduce_kernel(const float* __restrict__ part, int B,
+                                                           int blk, int Hkv,
+                                                           float* __restrict__ delta,
+                                                           int fuse_select, SelectArgs sel) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= B) return;  // uniform per wave
+  float sum = 0.f;
+  if (lane < blk) {
+    const float* pr = part + (size_t)r * Hkv * blk + lane;
+    for (int g = 0; g < Hkv; ++g) sum += pr[(size_t)g * blk];
+    delta[(size_t)r * blk + lane] = sum;
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(counters + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             Hkv - 1;
-  __syncthreads();
-  if (!s_last) return;
-  if (tid < BLK) {
-    const float* pr = part + (size_t)r * Hkv * BLK + tid;
-    float sum = 0.f;
-    for (int gg = 0; gg < Hkv; ++gg)
-      sum += __hip_atomic_load(pr + (size_t)gg * BLK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    delta[(size_t)r * BLK + tid] = sum;
-  }
-  if (tid == 0) __hip_atomic_store(counters + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (fuse_select) select_request(sel, r, sum, lane);
 }
 
 template <typename T, int BLK, int D, int GS>
@@ -252,12 +248,15 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
   if (a.lse0 != nullptr)
     hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS, true>), dim3(a.B * a.Hkv), dim3(256),
                        shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1,
-                       a.Hq, a.Hkv, a.scale_log2, a.lse0, a.lse1, a.part, a.counters, a.delta);
+                       a.Hq, a.Hkv, a.scale_log2, a.lse0, a.lse1, a.part);
   else
     hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS, false>), dim3(a.B * a.Hkv),
                        dim3(256), shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1,
-                       (const T*)a.k1, a.Hq, a.Hkv, a.scale_log2, nullptr, nullptr, a.part,
-                       a.counters, a.delta);
+                       (const T*)a.k1, a.Hq, a.Hkv, a.scale_log2, nullptr, nullptr, a.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(score_reduce_kernel, dim3((a.B + 3) / 4), dim3(256), 0, s, a.part, a.B,
+                     a.blk, a.Hkv, a.delta, a.fuse_select, a.sel);
   return hipGetLastError();
 }
 
@@ -290,7 +289,7 @@ hipError_t launch_dt(const ScoreArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t score_workspace_bytes(int B, int blk, int Hkv) {
-  return score_counter_bytes(B) + (size_t)B * Hkv * blk * sizeof(float);
+  return (size_t)B * Hkv * blk * sizeof(float);
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {

@@ -90,7 +90,27 @@ class FocusStep:
                             i.prefix_len, i.k_blk, i.v_blk, i.max_kept, i.sm_scale, out=self.out,
                             lse=self.lse, want_lse=self.lse is not None, workspace=self.ws_attn)
 
+    def score_select(self):
+        i = self.inp
+        F.score_select(i.q0, i.k0, i.q1, i.k1, i.sm_scale, i.masked, i.budget, i.adaptive,
+                       delta=self.delta, keep=self.keep, kept_count=self.kept_count,
+                       workspace=self.ws_score)
+
+    def compact(self):
+        sets = [self.inp.q_att] if self.inp.hidden is None else [self.inp.hidden, self.inp.q_att]
+        outs = [self.q_rows] if self.inp.hidden is None else [self.hidden_rows, self.q_rows]
+        F.compact_multi(self.keep, sets, self.cap, offsets=self.offsets, kept_pos=self.kept_pos,
+                        gathered=outs)
+
     def run(self):
+        """Three launches: score + select, compaction of the hidden states and the queries,
+        attention."""
+        self.score_select()
+        self.compact()
+        self.attend()
+
+    def run_unfused(self):
+        """The same step as five separate calls (one per entry point of the path)."""
         self.score()
         self.select()
         self.compact_hidden()

@@ -61,10 +61,9 @@ int focus_version(void);
  *   k0, k1      [B, blk, Hkv, d]  layer-0 / layer-1 block keys,    dtype `dtype`
  *   dtype       FOCUS_F32 or FOCUS_BF16 (products accumulate in f32)
  *   delta       [B, blk] f32 output
- *   workspace   device scratch of at least focus_score_l01_workspace_size(...) bytes,
- *               ZERO-FILLED before its first use (it holds per-request arrival counters that
- *               every call leaves at zero again, plus per-kv-head partial sums); calls that share
- *               a workspace must not run concurrently
+ *   workspace   device scratch of at least focus_score_l01_workspace_size(...) bytes (per-kv-head
+ *               partial sums; no initialisation); calls that share a workspace must not run
+ *               concurrently
  * Supported: blk in {16,32,64}; d in {64,128}; Hq % Hkv == 0; Hq/Hkv in {1,2,4,8};
  *            1 <= B <= 4096; Hkv <= 64.  Pointers must be 16-byte aligned.
  * ------------------------------------------------------------------------------------------ */
@@ -116,6 +115,20 @@ int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t
                         int32_t* kept_count, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------------
+ * 2b. Scoring and selection in one launch.
+ *
+ * The same results as focus_score_l01 followed by focus_select_budget with the same arguments
+ * (delta is written too): the kernel that completes each request's importance runs the request's
+ * selection right away, saving a launch and a round trip of delta through memory.
+ * Arguments, workspace and supported set: the union of the two calls'.
+ * ------------------------------------------------------------------------------------------ */
+int focus_score_select(const void* q0, const void* k0, const void* q1, const void* k1,
+                       int dtype, int B, int blk, int Hq, int Hkv, int d, float sm_scale,
+                       const uint8_t* masked, const int32_t* budget, int adaptive, float beta,
+                       int lo, int hi, float* delta, uint8_t* keep, int32_t* kept_count,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
  * 3. Compaction + gather (state compaction, ragged execution).
  *
  * Defined by the AI Engineering Academy article's "Arquitetura do FOCUS" section (the state is
@@ -138,6 +151,15 @@ int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t
 int focus_compact(const uint8_t* keep, int B, int blk, const void* rows, int64_t row_bytes,
                   int cap, int32_t* offsets, int32_t* kept_pos, void* gathered,
                   hipStream_t stream);
+
+/* Compaction gathering several row sets at once (e.g. the hidden states and the attention
+ * queries): the same as focus_compact on each set, offsets/kept_pos written once.
+ *   rows[s], row_bytes[s], gathered[s] for s < nsets: HOST arrays of device pointers / sizes
+ *   (read during the call only); each set as in focus_compact.
+ * Supported: 0 <= nsets <= 2, otherwise as focus_compact. */
+int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const void* const* rows,
+                        const int64_t* row_bytes, void* const* gathered, int cap,
+                        int32_t* offsets, int32_t* kept_pos, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------------
  * 4. Ragged paged attention of the kept queries.

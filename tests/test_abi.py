@@ -67,7 +67,7 @@ def test_score_errors():
     assert _score(q1=P + 8) == F.FOCUS_ERR_INVALID_ARG       # misaligned
     assert _score(ws=None) == F.FOCUS_ERR_WORKSPACE
     need = F.lib().focus_score_l01_workspace_size(4, 32, 32, 8, 128)
-    assert need == 256 + 4 * 8 * 32 * 4   # per-request counters (256-byte block) + partial sums
+    assert need == 4 * 8 * 32 * 4   # per-kv-head partial sums
     assert _score(wsb=need - 1) == F.FOCUS_ERR_WORKSPACE
 
 

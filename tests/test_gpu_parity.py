@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle as O
+from decodability_aware_token_amd import FocusStep
 from decodability_aware_token_amd import binding as F
 from parity_helpers import (DELTA_TOL, LSE_TOL, OUT_TOL, attn_case_inputs, bf16_to_np,
                             check_keep, compare_attention, oracle_attention, run_gpu_step,
@@ -562,3 +563,29 @@ def test_block_commit_failures_change_nothing():
         assert np.array_equal(d["po"].cpu().numpy(), plen)
         assert np.array_equal(d["pt"].cpu().numpy(), table)
         assert np.array_equal(_bits(d["kc"]), kc) and np.array_equal(_bits(d["vc"]), vc)
+
+
+@pytest.mark.parametrize("name,over", [("sdar_b256_blk32", {"B": 24}),
+                                       ("sweep_b128_blk64", {"B": 10}),
+                                       ("tiny_b2_blk16", {})])
+def test_fused_step_equals_separate_calls(name, over):
+    # score+select in one launch and both gathers in one compaction launch give exactly the
+    # results of the five separate entry points
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"fused vs separate {name} {over}")
+    from parity_helpers import fetch
+    fs = FocusStep(step_inputs(st))
+    fs.run_unfused()
+    torch.cuda.synchronize()
+    a = fetch(fs)
+    for nm in ("out", "delta", "q_rows", "hidden_rows", "keep", "kept_count", "offsets"):
+        t = getattr(fs, nm)
+        if t is not None:
+            t.fill_(0)
+    fs.run()
+    torch.cuda.synchronize()
+    b = fetch(fs)
+    for key in ("delta", "keep", "kept_count", "offsets", "kept_pos", "out_bits", "lse",
+                "hidden_rows"):
+        if key in a:
+            assert np.array_equal(a[key], b[key]), key
