@@ -207,11 +207,28 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
   }
 }
 
-// Loads the B operand (Q^T) of the cursor's item.  Rows past the item's rows (or past cap) are
+// The B operand (Q^T) of the current item.  With up to two query tiles it lives in registers;
+// with four (64 rows) it lives in the wave's slice of LDS, which keeps the QT = 4 kernel within
+// its registers (o alone takes 128, the two tile buffers another 128).
+template <int D, int QT>
+struct QOperand {
+  static constexpr int NK = D / 32;
+  static constexpr bool kLds = QT >= 4;
+  u32x4_t r[kLds ? 1 : QT][kLds ? 1 : NK];
+  u32x4_t* lds;  // [QT][NK][64 lanes] when kLds
+  __device__ __forceinline__ u32x4_t get(int qt, int kk, int lane) const {
+    if constexpr (kLds)
+      return lds[(qt * NK + kk) * 64 + lane];
+    else
+      return r[qt][kk];
+  }
+};
+
+// Loads the Q operand of the cursor's item.  Rows past the item's rows (or past cap) are
 // clamped to a valid row: their results are never written, and finite inputs keep them finite.
 template <int D, int QT>
-__device__ __forceinline__ void load_q(u32x4_t (&qf)[QT][D / 32], const Cursor& c,
-                                       const Params& p, int lane) {
+__device__ __forceinline__ void load_q(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
+                                       int lane) {
   constexpr int NK = D / 32, R = 16 * QT;
   const int m16 = lane & 15, j4 = lane >> 4;
 #pragma unroll
@@ -220,14 +237,22 @@ __device__ __forceinline__ void load_q(u32x4_t (&qf)[QT][D / 32], const Cursor& 
     const int tok = min(c.off0 + (rho >> p.log2G), p.cap - 1);
     const uint16_t* qrow =
         p.q + ((size_t)tok * p.Hq + c.g * p.G + (rho & (p.G - 1))) * D + 8 * j4;
+    if constexpr (QOperand<D, QT>::kLds) {
+      u32x4_t t[NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qf[qt][kk] = load16v(qrow + 32 * kk);
+      for (int kk = 0; kk < NK; ++kk) t[kk] = load16v(qrow + 32 * kk);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) qf.lds[(qt * NK + kk) * 64 + lane] = t[kk];
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) qf.r[qt][kk] = load16v(qrow + 32 * kk);
+    }
   }
 }
 
 template <int D, int QT>
 __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
-                                             const u32x4_t (&qf)[QT][D / 32],
+                                             const QOperand<D, QT>& qf,
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
                                              float (&lrun)[QT], float scale_log2, int lane) {
   constexpr int NK = D / 32, ND = D / 16;
@@ -248,8 +273,9 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      s0 = mfma_bf16(T.k[0][kk], qf[qt][kk], s0);
-      s1 = mfma_bf16(T.k[1][kk], qf[qt][kk], s1);
+      const u32x4_t q = qf.get(qt, kk, lane);
+      s0 = mfma_bf16(T.k[0][kk], q, s0);
+      s1 = mfma_bf16(T.k[1][kk], q, s1);
     }
     float x[8];
 #pragma unroll
@@ -318,6 +344,9 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
   meta.off = meta.P + B;
   meta.rows = meta.off + B;
   int* s_part = meta.rows + B;  // [256]
+  // per-wave Q operand (QT = 4 only), 16-byte aligned after the metadata
+  unsigned char* s_q = reinterpret_cast<unsigned char*>(smem_i) +
+                       ((((size_t)4 * B + 1 + 256) * sizeof(int) + 15) & ~(size_t)15);
   const int per = (B + 255) / 256;
   int local = 0;
   for (int i = 0; i < per; ++i) {
@@ -570,7 +599,9 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
   // stays on the last tile, so the prefetch is unconditional (it re-reads that tile: cache
   // hits).  When C starts a piece its queries are loaded before the next prefetch, so the
   // compute's wait does not drain the tiles in flight.
-  u32x4_t qf[QT][NK];
+  QOperand<D, QT> qf;
+  if constexpr (QOperand<D, QT>::kLds)
+    qf.lds = reinterpret_cast<u32x4_t*>(s_q) + (size_t)wave * QT * NK * 64;
   load_q<D, QT>(qf, C, p, lane);
   Cursor L = C;
   int tvl = 0, tvc = 0;  // processing indices of L and C
@@ -644,7 +675,8 @@ int device_cus() {
 
 template <int D, int QT>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
-  const size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
+  size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
+  if (QT >= 4) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
   constexpr int NB = QT == 1 ? kPrefetchQt1 : 2;
   hipLaunchKernelGGL((attn_kernel<D, QT, NB>), dim3(plan.wgs), dim3(256), shmem, s, prm,
                      prm.page_table);
