@@ -214,7 +214,8 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
                             const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
                             int max_kept, float sm_scale, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !offsets || !prefix_len || !k_blk || !v_blk || !out) return FOCUS_ERR_INVALID_ARG;
+  if (!offsets || !prefix_len || !k_blk || !v_blk) return FOCUS_ERR_INVALID_ARG;
+  if (cap > 0 && (!q || !out)) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || S <= 0 || cap < 0 ||
       num_pages < 0 || max_pages < 0 || max_kept <= 0)
     return FOCUS_ERR_INVALID_ARG;

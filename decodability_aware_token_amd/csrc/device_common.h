@@ -59,14 +59,20 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // waits until every vector memory access of the wave, stores included, has completed
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Global-memory views of device pointers: loads through them are global (never flat)
+// instructions, which the compiler's wait counting can order with the other vector loads
+// (a pending flat load makes every later wait a full drain).
+typedef const __attribute__((address_space(1))) u32x2_t global_u32x2_t;
+typedef const __attribute__((address_space(1))) u32x4_t global_u32x4_t;
+
 // 8-byte load of data read exactly once (non-temporal: the caches do not keep it)
 __device__ __forceinline__ u32x2_t load8_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return __builtin_nontemporal_load((global_u32x2_t*)p);
 }
 
 // 16-byte load of data read exactly once (non-temporal: the caches do not keep it)
 __device__ __forceinline__ u32x4_t load16_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return __builtin_nontemporal_load((global_u32x4_t*)p);
 }
 
 }  // namespace focus

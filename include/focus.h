@@ -180,6 +180,7 @@ int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const vo
  *   page_table [B, max_pages] i32: prefix token t of request r is in page page_table[r, t/S]
  *   prefix_len [B] i32
  *   q   [cap, Hq, d] bf16 (compacted queries)   out [cap, Hq, d] bf16   lse [cap, Hq] f32 or NULL
+ *   (q and out may be NULL when cap == 0: the call then only checks its arguments)
  * max_kept is an upper bound of every kept count (offsets[r+1]-offsets[r]); it sizes the
  * launch.  Rows t >= max_kept of a request are not written.  Rows n >= cap are not read or
  * written.  Device data the host cannot check: a request whose prefix_len is negative or above
@@ -187,8 +188,9 @@ int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const vo
  * rows instead of a memory access.
  *   workspace   at least focus_ragged_paged_attn_workspace_size(...) bytes, ZERO-FILLED before its
  *               first use (it holds arrival counters that every call leaves at zero again, plus
- *               per-wave partial results); calls that share a workspace must not run
- *               concurrently.  The size depends on the current device's compute-unit count.
+ *               per-wave partial results).  Calls that share a workspace must not run
+ *               concurrently; calls of different shapes may share one.  The size depends on the
+ *               current device's compute-unit count.
  * Supported: d in {64,128}; S in {16,32,64}; blk in {16,32,64}; Hq/Hkv in {1,2,4,8};
  *            1 <= max_kept <= blk; 1 <= B <= 4096; max_pages*S <= 2^24; fewer than 2^31 key
  *            tiles of 32 over all (request, kv head, query group) at the longest prefixes;

@@ -163,6 +163,9 @@ def test_attn_errors():
     assert need > 0
     assert _attn(maxp=128, ws=None) == F.FOCUS_ERR_WORKSPACE
     assert _attn(maxp=128, wsb=need - 1) == F.FOCUS_ERR_WORKSPACE
+    # nothing kept: no query or output rows, nothing launched
+    assert _attn(cap=0, q=None, out=None) == F.FOCUS_OK
+    assert _attn(cap=0, q=None, out=None, S=48) == F.FOCUS_ERR_UNSUPPORTED
 
 
 def test_attn_plan_is_bounded():
