@@ -377,7 +377,7 @@ def main():
 
     # Pass 1 (eager, per-stage HIP events on the launch stream): the stage breakdown and the
     # attention kernel's launch duration for the roofline.
-    stages = ("score_select", "compact", "attend")
+    stages = fs.front_stages + ("attend",)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
     log(f"[bench] eager pass: {args.steps} steps with per-stage events")
@@ -399,9 +399,9 @@ def main():
     per_stage /= args.steps
     eager_ms = eager_wall * 1000.0 / args.steps
 
-    # Pass 2 (the measured step): the whole step (three launches: score + select, compaction of
-    # the hidden states and queries, attention) captured once in a HIP graph, W untimed
-    # replays, then exactly K replays between device synchronisations.
+    # Pass 2 (the measured step): the whole step (score partials, reduction + selection +
+    # compaction of the hidden states and queries, attention) captured once in a HIP graph, W
+    # untimed replays, then exactly K replays between device synchronisations.
     ms_per_step = eager_ms
     mode = "eager"
     if not args.no_graph:
@@ -433,8 +433,8 @@ def main():
         f"({achieved / PEAK_HBM_GBS * 100:.1f}% of HBM), "
         f"{attn_flops / (attn_ms * 1e-3) / 1e12:.2f} TFLOP/s")
     sc_ms = per_stage[0]
-    log(f"[bench] score+select {sb / 1e6:.1f} MB -> {sb / (sc_ms * 1e-3) / 1e9:.0f} GB/s, "
-        f"{sf / (sc_ms * 1e-3) / 1e12:.2f} TFLOP/s")
+    log(f"[bench] {stages[0]}: score inputs {sb / 1e6:.1f} MB -> "
+        f"{sb / (sc_ms * 1e-3) / 1e9:.0f} GB/s, {sf / (sc_ms * 1e-3) / 1e12:.2f} TFLOP/s")
 
     full = None
     if not args.no_full_block:

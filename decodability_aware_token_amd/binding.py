@@ -55,6 +55,10 @@ SIGNATURES = {
                                                                   _c_void_p]),
     "focus_compact_multi": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                      _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "focus_score_select_compact": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 +
+                                   [_c_float] + [_c_void_p] * 5 + [_c_int] +
+                                   [_c_void_p] * 3 + [_c_int] + [_c_void_p] * 2 + [_c_int] +
+                                   [_c_void_p, _c_size_t, _c_void_p]),
     "focus_kv_writeback": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p] * 3),
     "focus_block_commit": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 2 +
                            [_c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -277,6 +281,51 @@ def score_select(q0, k0, q1, k1, sm_scale: float, masked, budget=None, adaptive=
     return delta, keep, kept_count
 
 
+def _row_set_arrays(row_sets, gathered):
+    if not all(t.is_contiguous() for t in list(row_sets) + list(gathered)):
+        raise ValueError("tensors handed to libfocus must be contiguous")
+    n = len(row_sets)
+    rows_arr = (_c_void_p * max(n, 1))(*[r.data_ptr() for r in row_sets])
+    bytes_arr = (_c_int64 * max(n, 1))(*[r[0, 0].numel() * r.element_size() for r in row_sets])
+    out_arr = (_c_void_p * max(n, 1))(*[g.data_ptr() for g in gathered])
+    return rows_arr, bytes_arr, out_arr
+
+
+def score_select_compact(q0, k0, q1, k1, sm_scale: float, masked, budget, row_sets, cap: int,
+                         max_kept=None, delta=None, keep=None, kept_count=None, offsets=None,
+                         kept_pos=None, gathered=None, workspace=None):
+    """delta, keep, kept_count, offsets, kept_pos and the gathered row sets of
+    focus_score_select with per-request budgets followed by focus_compact_multi, in two launches
+    (see focus_score_select_compact)."""
+    B, blk, Hq, d = q0.shape
+    Hkv = k0.shape[2]
+    dev = q0.device
+    dt = {torch.float32: FOCUS_F32, torch.bfloat16: FOCUS_BF16}[q0.dtype]
+    if delta is None:
+        delta = torch.empty((B, blk), dtype=torch.float32, device=dev)
+    if keep is None:
+        keep = torch.empty((B, blk), dtype=torch.uint8, device=dev)
+    if kept_count is None:
+        kept_count = torch.empty(B, dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if kept_pos is None:
+        kept_pos = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if gathered is None:
+        gathered = [torch.empty((max(cap, 1),) + tuple(r.shape[2:]), dtype=r.dtype, device=dev)
+                    for r in row_sets]
+    rows_arr, bytes_arr, out_arr = _row_set_arrays(row_sets, gathered)
+    need = lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
+    workspace, wsb = _workspace(need, dev, workspace)
+    rc = lib().focus_score_select_compact(
+        _ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), dt, B, blk, Hq, Hkv, d, float(sm_scale),
+        _ptr(masked), _ptr(budget), _ptr(delta), _ptr(keep), _ptr(kept_count), len(row_sets),
+        rows_arr, bytes_arr, out_arr, int(cap), _ptr(offsets), _ptr(kept_pos),
+        int(blk if max_kept is None else max_kept), _ptr(workspace), wsb, _stream(dev))
+    _check("focus_score_select_compact", rc)
+    return delta, keep, kept_count, offsets, kept_pos, gathered
+
+
 def compact_multi(keep, row_sets, cap: int, offsets=None, kept_pos=None, gathered=None):
     """offsets, kept_pos and one gathered tensor per row set [B, blk, ...] (see
     focus_compact_multi); ``gathered`` optionally gives the output tensors."""
@@ -290,11 +339,7 @@ def compact_multi(keep, row_sets, cap: int, offsets=None, kept_pos=None, gathere
     if gathered is None:
         gathered = [torch.empty((max(cap, 1),) + tuple(r.shape[2:]), dtype=r.dtype, device=dev)
                     for r in row_sets]
-    if not all(t.is_contiguous() for t in list(row_sets) + list(gathered)):
-        raise ValueError("tensors handed to libfocus must be contiguous")
-    rows_arr = (_c_void_p * max(n, 1))(*[r.data_ptr() for r in row_sets])
-    bytes_arr = (_c_int64 * max(n, 1))(*[r[0, 0].numel() * r.element_size() for r in row_sets])
-    out_arr = (_c_void_p * max(n, 1))(*[g.data_ptr() for g in gathered])
+    rows_arr, bytes_arr, out_arr = _row_set_arrays(row_sets, gathered)
     rc = lib().focus_compact_multi(_ptr(keep), B, blk, n, rows_arr, bytes_arr, out_arr, int(cap),
                                    _ptr(offsets), _ptr(kept_pos), _stream(dev))
     _check("focus_compact_multi", rc)

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "launch.h"
@@ -50,11 +51,11 @@ size_t focus_score_l01_workspace_size(int B, int blk, int Hq, int Hkv, int d) {
 }
 
 namespace {
-int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
-                 const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
-                 int Hkv, int d, float sm_scale, float* delta, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream,
-                 const focus::SelectArgs* sel = nullptr) {
+// Validates the scoring arguments and fills a; FOCUS_OK or the error code.
+int score_prepare(const void* q0, const void* k0, const void* q1, const void* k1,
+                  const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
+                  int Hkv, int d, float sm_scale, float* delta, void* workspace,
+                  size_t workspace_bytes, focus::ScoreArgs& a) {
   if (!q0 || !k0 || !q1 || !k1 || !delta) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FOCUS_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return FOCUS_ERR_INVALID_ARG;
@@ -67,7 +68,7 @@ int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
   if (lse0 && (!aligned4(lse0) || !aligned4(lse1))) return FOCUS_ERR_INVALID_ARG;
   const size_t need = focus::score_workspace_bytes(B, blk, Hkv);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FOCUS_ERR_WORKSPACE;
-  focus::ScoreArgs a{};
+  a = focus::ScoreArgs{};
   a.q0 = q0;
   a.k0 = k0;
   a.q1 = q1;
@@ -83,6 +84,18 @@ int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
   a.lse1 = lse1;
   a.delta = delta;
   a.part = static_cast<float*>(workspace);
+  return FOCUS_OK;
+}
+
+int score_common(const void* q0, const void* k0, const void* q1, const void* k1,
+                 const float* lse0, const float* lse1, int dtype, int B, int blk, int Hq,
+                 int Hkv, int d, float sm_scale, float* delta, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream,
+                 const focus::SelectArgs* sel = nullptr) {
+  focus::ScoreArgs a;
+  const int rc = score_prepare(q0, k0, q1, k1, lse0, lse1, dtype, B, blk, Hq, Hkv, d, sm_scale,
+                               delta, workspace, workspace_bytes, a);
+  if (rc != FOCUS_OK) return rc;
   if (sel) {
     a.fuse_select = 1;
     a.sel = *sel;
@@ -155,15 +168,15 @@ int focus_select_budget(const float* delta, const uint8_t* masked, const int32_t
 }
 
 namespace {
-int compact_common(const uint8_t* keep, int B, int blk, int nsets, const void* const* rows,
-                   const int64_t* row_bytes, void* const* gathered, int cap, int32_t* offsets,
-                   int32_t* kept_pos, hipStream_t stream) {
-  if (!keep || !offsets) return FOCUS_ERR_INVALID_ARG;
+// Validates the compaction arguments other than keep and fills a (keep left null).
+int compact_prepare(int B, int blk, int nsets, const void* const* rows, const int64_t* row_bytes,
+                    void* const* gathered, int cap, int32_t* offsets, int32_t* kept_pos,
+                    focus::CompactArgs& a) {
+  if (!offsets) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || cap < 0 || nsets < 0) return FOCUS_ERR_INVALID_ARG;
   if (nsets > 0 && (!rows || !row_bytes || !gathered)) return FOCUS_ERR_INVALID_ARG;
-  if (!aligned4(keep)) return FOCUS_ERR_INVALID_ARG;
   if (!pow2_in(blk, 16, 64) || B > kMaxB || nsets > focus::kMaxSets) return FOCUS_ERR_UNSUPPORTED;
-  focus::CompactArgs a{};
+  a = focus::CompactArgs{};
   for (int si = 0; si < nsets; ++si) {
     if (!rows[si] || !gathered[si] || row_bytes[si] <= 0) return FOCUS_ERR_INVALID_ARG;
     if (row_bytes[si] % 16 != 0 || row_bytes[si] > kMaxRowBytes || !aligned16(rows[si]) ||
@@ -173,13 +186,25 @@ int compact_common(const uint8_t* keep, int B, int blk, int nsets, const void* c
     a.row_bytes[si] = row_bytes[si];
     a.gathered[si] = gathered[si];
   }
-  a.keep = keep;
   a.B = B;
   a.blk = blk;
   a.nsets = nsets;
   a.cap = cap;
   a.offsets = offsets;
   a.kept_pos = kept_pos;
+  return FOCUS_OK;
+}
+
+int compact_common(const uint8_t* keep, int B, int blk, int nsets, const void* const* rows,
+                   const int64_t* row_bytes, void* const* gathered, int cap, int32_t* offsets,
+                   int32_t* kept_pos, hipStream_t stream) {
+  if (!keep) return FOCUS_ERR_INVALID_ARG;
+  focus::CompactArgs a;
+  const int rc =
+      compact_prepare(B, blk, nsets, rows, row_bytes, gathered, cap, offsets, kept_pos, a);
+  if (rc != FOCUS_OK) return rc;
+  if (!aligned4(keep)) return FOCUS_ERR_INVALID_ARG;
+  a.keep = keep;
   return status_of(focus::launch_compact(a, stream));
 }
 }  // namespace
@@ -198,6 +223,47 @@ int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const vo
                         int32_t* offsets, int32_t* kept_pos, hipStream_t stream) {
   return compact_common(keep, B, blk, nsets, rows, row_bytes, gathered, cap, offsets, kept_pos,
                         stream);
+}
+
+int focus_score_select_compact(const void* q0, const void* k0, const void* q1, const void* k1,
+                               int dtype, int B, int blk, int Hq, int Hkv, int d, float sm_scale,
+                               const uint8_t* masked, const int32_t* budget, float* delta,
+                               uint8_t* keep, int32_t* kept_count, int nsets,
+                               const void* const* rows, const int64_t* row_bytes,
+                               void* const* gathered, int cap, int32_t* offsets,
+                               int32_t* kept_pos, int max_kept, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (!masked || !budget || !keep || !kept_count) return FOCUS_ERR_INVALID_ARG;
+  if (max_kept < 1 || max_kept > blk) return FOCUS_ERR_INVALID_ARG;
+  focus::ScoreArgs sa;
+  int rc = score_prepare(q0, k0, q1, k1, nullptr, nullptr, dtype, B, blk, Hq, Hkv, d, sm_scale,
+                         delta, workspace, workspace_bytes, sa);
+  if (rc != FOCUS_OK) return rc;
+  focus::CompactArgs ca;
+  rc = compact_prepare(B, blk, nsets, rows, row_bytes, gathered, cap, offsets, kept_pos, ca);
+  if (rc != FOCUS_OK) return rc;
+  if (!aligned4(masked)) return FOCUS_ERR_INVALID_ARG;
+  sa.partial_only = 1;
+  hipError_t e = focus::launch_score(sa, stream);
+  if (e != hipSuccess) return FOCUS_ERR_HIP;
+  focus::SelectCompactArgs a{};
+  a.part = sa.part;
+  a.Hkv = Hkv;
+  a.delta = delta;
+  a.sel.masked = masked;
+  a.sel.budget = budget;
+  a.sel.adaptive = 0;
+  a.sel.B = B;
+  a.sel.blk = blk;
+  a.sel.keep = keep;
+  a.sel.kept_count = kept_count;
+  a.cmp = ca;
+  // workgroups per request: one 32 KiB gather batch each for max_kept rows of every set
+  int64_t bytes = 0;
+  for (int si = 0; si < nsets; ++si) bytes += row_bytes[si];
+  const int64_t per_wg = 256 * 8 * 16;
+  a.nsplit = (int)std::min<int64_t>(16, std::max<int64_t>(1, (max_kept * bytes + per_wg - 1) / per_wg));
+  return status_of(focus::launch_select_compact(a, stream));
 }
 
 size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, int d, int S,

@@ -33,6 +33,7 @@ struct ScoreArgs {
   float* part;       // workspace [B, Hkv, blk]
   int fuse_select;   // run the selection of each request right after its delta
   SelectArgs sel;    // (delta unused: the request's delta is in registers)
+  int partial_only;  // stop after the per-kv-head partials (a later kernel reduces them)
 };
 size_t score_workspace_bytes(int B, int blk, int Hkv);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
@@ -52,6 +53,17 @@ struct CompactArgs {
   int32_t* kept_pos;
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+// Reduction of the score partials + selection with caller budgets + compaction, one launch.
+struct SelectCompactArgs {
+  const float* part;  // [B, Hkv, blk] score partials
+  int Hkv;
+  float* delta;       // [B, blk] output
+  SelectArgs sel;     // masked, budget, keep, kept_count, B, blk (adaptive = 0)
+  CompactArgs cmp;    // row sets, cap, offsets, kept_pos (keep unused)
+  int nsplit;         // workgroups per request (each gathers a share of its rows), 1..16
+};
+hipError_t launch_select_compact(const SelectCompactArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t* q;

@@ -254,7 +254,7 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
                        dim3(256), shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1,
                        (const T*)a.k1, a.Hq, a.Hkv, a.scale_log2, nullptr, nullptr, a.part);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.partial_only) return e;
   hipLaunchKernelGGL(score_reduce_kernel, dim3((a.B + 3) / 4), dim3(256), 0, s, a.part, a.B,
                      a.blk, a.Hkv, a.delta, a.fuse_select, a.sel);
   return hipGetLastError();

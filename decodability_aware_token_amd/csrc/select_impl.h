@@ -25,8 +25,15 @@ __device__ __forceinline__ float wave_sum_all(float v) {
   return v;
 }
 
-// Every lane of the wave must call this (lanes >= blk pass any dj).
-__device__ __forceinline__ void select_request(const SelectArgs& a, int r, float dj, int lane) {
+struct Selection {
+  bool kept;  // this lane's position is kept
+  int k;      // the request's kept count
+};
+
+// Every lane of the wave must call this (lanes >= blk pass any dj).  Reads the request's mask
+// (and budget) and returns the decision; stores nothing.
+__device__ __forceinline__ Selection select_compute(const SelectArgs& a, int r, float dj,
+                                                    int lane) {
   const int blk = a.blk;
   const bool in_blk = lane < blk;
   const bool mj = in_blk && a.masked[(size_t)r * blk + lane] != 0;
@@ -53,8 +60,14 @@ __device__ __forceinline__ void select_request(const SelectArgs& a, int r, float
     const bool mi = (mbits >> i) & 1ull;
     rank += (mi && (di > dj || (di == dj && i < lane))) ? 1 : 0;
   }
-  if (in_blk) a.keep[(size_t)r * blk + lane] = (mj && rank < k) ? 1 : 0;
-  if (lane == 0) a.kept_count[r] = k;
+  return Selection{mj && rank < k, k};
+}
+
+// Every lane of the wave must call this (lanes >= blk pass any dj).
+__device__ __forceinline__ void select_request(const SelectArgs& a, int r, float dj, int lane) {
+  const Selection sel = select_compute(a, r, dj, lane);
+  if (lane < a.blk) a.keep[(size_t)r * a.blk + lane] = sel.kept ? 1 : 0;
+  if (lane == 0) a.kept_count[r] = sel.k;
 }
 
 }  // namespace focus

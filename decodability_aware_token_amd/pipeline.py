@@ -1,8 +1,10 @@
 """One focused block-diffusion step on the GPU: score -> select -> compact (hidden, Q) -> attend.
 
 `FocusStep` preallocates every output and workspace once for a fixed batch shape, then `run()`
-issues the four C-ABI calls back to back on the current stream with no host synchronisation:
-ragged sizes stay on the device, and the attention is sized by the host-known bound max_kept.
+issues the C-ABI calls back to back on the current stream with no host synchronisation: ragged
+sizes stay on the device, and the attention is sized by the host-known bound max_kept.  With
+per-request budgets the front end (score, select, compact) is one call of two launches; with the
+adaptive rule it is two calls (score + select, then compaction).
 `capture()` records one step into a HIP graph (no allocation, no memset node: the kernels reset
 their own arrival counters), and `replay()` launches it, which removes the per-kernel launch
 gaps of the eager path.
@@ -97,16 +99,38 @@ class FocusStep:
                        workspace=self.ws_score)
 
     def compact(self):
-        sets = [self.inp.q_att] if self.inp.hidden is None else [self.inp.hidden, self.inp.q_att]
-        outs = [self.q_rows] if self.inp.hidden is None else [self.hidden_rows, self.q_rows]
+        sets, outs = self._row_sets()
         F.compact_multi(self.keep, sets, self.cap, offsets=self.offsets, kept_pos=self.kept_pos,
                         gathered=outs)
 
+    def _row_sets(self):
+        sets = [self.inp.q_att] if self.inp.hidden is None else [self.inp.hidden, self.inp.q_att]
+        outs = [self.q_rows] if self.inp.hidden is None else [self.hidden_rows, self.q_rows]
+        return sets, outs
+
+    def score_select_compact(self):
+        """Score partials, then reduction + selection + compaction in one launch (per-request
+        budgets only)."""
+        i = self.inp
+        sets, outs = self._row_sets()
+        F.score_select_compact(i.q0, i.k0, i.q1, i.k1, i.sm_scale, i.masked, i.budget, sets,
+                               self.cap, max_kept=i.max_kept, delta=self.delta, keep=self.keep,
+                               kept_count=self.kept_count, offsets=self.offsets,
+                               kept_pos=self.kept_pos, gathered=outs, workspace=self.ws_score)
+
+    @property
+    def front_stages(self):
+        """The calls of the step before the attention."""
+        if self.inp.adaptive is None:
+            return ("score_select_compact",)
+        return ("score_select", "compact")
+
     def run(self):
-        """Three launches: score + select, compaction of the hidden states and the queries,
-        attention."""
-        self.score_select()
-        self.compact()
+        """The front end (two launches with per-request budgets: score partials, then
+        reduction + selection + compaction; three with the adaptive rule: score + select,
+        compaction), then the attention."""
+        for name in self.front_stages:
+            getattr(self, name)()
         self.attend()
 
     def run_unfused(self):

@@ -162,6 +162,29 @@ int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const vo
                         int32_t* offsets, int32_t* kept_pos, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------------
+ * 3b. Scoring, selection with per-request budgets and compaction in two launches.
+ *
+ * The same results as focus_score_select (adaptive == 0) followed by focus_compact_multi on its
+ * keep output: delta, keep, kept_count, offsets, kept_pos and the gathered rows.  With the
+ * caller's integer budgets, request r keeps k_r = min(max(budget[r], 0), m_r) tokens, a number
+ * known from the mask alone, so each request's place in the compacted order follows from the
+ * masks and budgets of the requests before it: the second launch reduces the importance,
+ * selects and gathers each request without waiting for the others.  (The adaptive rule needs
+ * every request's delta first: use focus_score_select and focus_compact_multi for it.)
+ * Arguments, workspace and supported set: those of the two calls; masked must be 4-byte
+ * aligned.  max_kept (1..blk) is the caller's bound of the kept counts: it sizes the launch
+ * (how many workgroups gather a request's rows), the results do not depend on it.
+ * ------------------------------------------------------------------------------------------ */
+int focus_score_select_compact(const void* q0, const void* k0, const void* q1, const void* k1,
+                               int dtype, int B, int blk, int Hq, int Hkv, int d, float sm_scale,
+                               const uint8_t* masked, const int32_t* budget, float* delta,
+                               uint8_t* keep, int32_t* kept_count, int nsets,
+                               const void* const* rows, const int64_t* row_bytes,
+                               void* const* gathered, int cap, int32_t* offsets,
+                               int32_t* kept_pos, int max_kept, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
  * 4. Ragged paged attention of the kept queries.
  *
  * Defined by the AI Engineering Academy article (ragged paged attention integrated with the

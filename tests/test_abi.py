@@ -130,6 +130,38 @@ def test_compact_errors():
     assert _compact(B=4097) == F.FOCUS_ERR_UNSUPPORTED
 
 
+def _ssc(**kw):
+    import ctypes
+    a = dict(q0=P, k0=P, q1=P, k1=P, dt=1, B=4, blk=32, Hq=32, Hkv=8, d=128, sc=0.1, msk=P,
+             bud=P, delta=P, keep=P, kc=P, n=1, rows=[P], rb=[8192], gat=[P], cap=128, off=P,
+             pos=P, mk=4, ws=P, wsb=1 << 30)
+    a.update(kw)
+    n = max(len(a["rows"]), 1)
+    rows = (ctypes.c_void_p * n)(*a["rows"])
+    rb = (ctypes.c_int64 * n)(*a["rb"])
+    gat = (ctypes.c_void_p * n)(*a["gat"])
+    return F.lib().focus_score_select_compact(
+        a["q0"], a["k0"], a["q1"], a["k1"], a["dt"], a["B"], a["blk"], a["Hq"], a["Hkv"], a["d"],
+        a["sc"], a["msk"], a["bud"], a["delta"], a["keep"], a["kc"], a["n"], rows, rb, gat,
+        a["cap"], a["off"], a["pos"], a["mk"], a["ws"], a["wsb"], None)
+
+
+def test_score_select_compact_errors():
+    assert _ssc(bud=None) == F.FOCUS_ERR_INVALID_ARG          # per-request budgets only
+    assert _ssc(msk=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc(keep=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc(q0=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc(off=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc(msk=P + 2) == F.FOCUS_ERR_INVALID_ARG         # masked must be 4-byte aligned
+    assert _ssc(blk=20) == F.FOCUS_ERR_UNSUPPORTED
+    assert _ssc(rb=[8200]) == F.FOCUS_ERR_UNSUPPORTED          # not a multiple of 16
+    assert _ssc(n=3, rows=[P] * 3, rb=[16] * 3, gat=[P] * 3) == F.FOCUS_ERR_UNSUPPORTED
+    assert _ssc(wsb=16) == F.FOCUS_ERR_WORKSPACE
+    assert _ssc(cap=-1) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc(mk=0) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc(mk=33) == F.FOCUS_ERR_INVALID_ARG             # max_kept > blk
+
+
 def _attn(**kw):
     a = dict(q=P, off=P, cap=64, kc=P, vc=P, npages=100, pt=P, maxp=16, pl=P, kb=P, vb=P, B=4,
              blk=32, Hq=32, Hkv=8, d=128, S=64, mk=4, sc=0.088, out=P, lse=P, ws=P,

@@ -607,3 +607,41 @@ def test_fused_step_equals_separate_calls(name, over):
                 "hidden_rows"):
         if key in a:
             assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name,over,cap_frac", [
+    ("tiny_b2_blk16", {}, 1.0),
+    ("sdar_b32_blk32", {"B": 300, "prefix": ("fixed", 64), "max_prefix": 64}, 1.0),
+    ("sdar_b32_blk32", {"B": 40, "prefix": ("fixed", 64), "max_prefix": 64}, 0.05),  # overflow
+    ("sweep_b128_blk16", {"B": 33, "prefix": ("fixed", 64), "max_prefix": 64}, 1.0),
+    ("sweep_b128_blk64", {"B": 21, "prefix": ("fixed", 64), "max_prefix": 64}, 1.0),
+])
+def test_score_select_compact_equals_two_calls(name, over, cap_frac):
+    # the two-launch front end with per-request budgets (including budgets below zero and above
+    # the masked count) gives exactly what score + select and the compaction give, also past
+    # the first 256 predecessors and when the kept rows overflow cap
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"score_select_compact {name} {over} cap_frac={cap_frac}")
+    t = step_inputs(st)
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + st.B)
+    budget = torch.from_numpy(rng.integers(-2, st.blk + 3, size=st.B).astype(np.int32)).cuda()
+    sets = [t.q_att] if t.hidden is None else [t.hidden, t.q_att]
+    cap = max(1, int(cap_frac * st.B * st.blk))
+    d1, k1, c1 = F.score_select(t.q0, t.k0, t.q1, t.k1, t.sm_scale, t.masked, budget)
+    o1, p1, g1 = F.compact_multi(k1, sets, cap)
+    torch.cuda.synchronize()
+    T = min(int(o1[-1]), cap)
+    # the launch bound max_kept changes how many workgroups gather, never the results (even when
+    # the budgets exceed it)
+    for mk in (1, 3, st.blk):
+        d2, k2, c2, o2, p2, g2 = F.score_select_compact(t.q0, t.k0, t.q1, t.k1, t.sm_scale,
+                                                        t.masked, budget, sets, cap, max_kept=mk)
+        torch.cuda.synchronize()
+        assert torch.equal(d1, d2) and torch.equal(k1, k2) and torch.equal(c1, c2)
+        assert torch.equal(o1, o2)
+        assert torch.equal(p1[:T], p2[:T])
+        for a, b in zip(g1, g2):
+            assert torch.equal(a[:T].view(torch.int16), b[:T].view(torch.int16))
+    # the kept counts follow the budgets: min(max(b, 0), masked count)
+    m = t.masked.ne(0).sum(1).to(torch.int32)
+    assert torch.equal(c2, torch.minimum(budget.clamp(min=0), m))
