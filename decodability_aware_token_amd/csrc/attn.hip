@@ -53,6 +53,9 @@ constexpr int kWgsPerCuQt1 = 1;
 constexpr int kCpolDevice = 16;
 // third word of a raw (unswizzled, 32-bit format) buffer resource
 constexpr int kRawBufferFormat = 0x00020000;
+// how far (log2 units) a row's logits may exceed its reference max before the running output
+// is rescaled: softmax weights stay below 2^8
+constexpr float kRescaleSlack = 8.f;
 
 struct Params {
   const uint16_t* q;
@@ -269,7 +272,12 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     vmask[w] = (b + 1 < n) ? 0xffffffffu : ((b < n) ? 0x0000ffffu : 0u);
   }
 #pragma unroll
+  for (int dt = 0; dt < ND; ++dt) T.v[dt] &= vmask;  // once per tile, in place
+#pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
+    // one query tile at a time: without the barrier the scheduler hoists every tile's operand
+    // reads and keeps them live, which with four tiles no longer fits the registers
+    if (QT > 2) __builtin_amdgcn_sched_barrier(0);
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
@@ -290,12 +298,21 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
-    const float mnew = fmaxf(mrun[qt], mx);
-    float alpha = 1.f, msub = 0.f;
-    if (mnew != -INFINITY) {
-      alpha = fast_exp2(mrun[qt] - mnew);
-      msub = mnew;
+    // The reference max of a row moves only when the tile's max exceeds it by more than
+    // kRescaleSlack (log2 units): then every row of the query tile is rescaled to its new max
+    // (o, l times exp2(old - new); o is still zero when the old max is -inf).  Otherwise the
+    // weights exp2(x - m) stay below 2^kRescaleSlack, which fp32 sums and bf16 weights hold
+    // without loss, and o needs no multiply: it is then touched by the matrix unit only.
+    if (__ballot(mx > mrun[qt] + kRescaleSlack) != 0) {
+      const float mnew = fmaxf(mrun[qt], mx);
+      const float alpha = mnew == -INFINITY || mrun[qt] == -INFINITY
+                              ? 0.f : fast_exp2(mrun[qt] - mnew);
+      lrun[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[qt][dt] *= alpha;
+      mrun[qt] = mnew;
     }
+    const float msub = mrun[qt] == -INFINITY ? 0.f : mrun[qt];
     float pe[8];
     float ls = 0.f;
 #pragma unroll
@@ -303,18 +320,14 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
       pe[e] = fast_exp2(x[e] - msub);
       ls += pe[e];
     }
-    lrun[qt] = lrun[qt] * alpha + ls;
-    mrun[qt] = mnew;
+    lrun[qt] += ls;
     u32x4_t pf;
     pf[0] = pack_bf16x2(pe[0], pe[1]);
     pf[1] = pack_bf16x2(pe[2], pe[3]);
     pf[2] = pack_bf16x2(pe[4], pe[5]);
     pf[3] = pack_bf16x2(pe[6], pe[7]);
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      o[qt][dt] *= alpha;
-      o[qt][dt] = mfma_bf16(T.v[dt] & vmask, pf, o[qt][dt]);
-    }
+    for (int dt = 0; dt < ND; ++dt) o[qt][dt] = mfma_bf16(T.v[dt], pf, o[qt][dt]);
   }
 }
 

@@ -234,6 +234,41 @@ def test_attn_peaky_inputs_and_cap():
     assert torch.all(sentinel[cap:] == 7.0)
 
 
+def test_attn_growing_logits_rescale():
+    # keys scaled up page by page along each prefix (and the block keys most): the running max
+    # of a row keeps jumping by many log2 units inside an item, so the output is rescaled
+    # several times per item and its weights span a wide range
+    st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=6))
+    _announce("attn growing logits")
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    kc = bf16_bits_to_f32(st.k_cache)
+    seen = set()
+    for r in range(st.B):
+        for i in range(int(np.ceil(st.prefix_len[r] / st.S))):
+            pid = int(st.page_table[r, i])
+            if pid not in seen:
+                seen.add(pid)
+                kc[pid] *= 1.0 + 3.0 * i
+    st.k_cache = f32_to_bf16_bits(kc)
+    st.k_blk = f32_to_bf16_bits(bf16_bits_to_f32(st.k_blk) * 24.0)
+    rng = np.random.default_rng(8)
+    keep = _random_keep(rng, st.B, st.blk, 4, empty_frac=0.0)
+    c = attn_case_inputs(st, keep)
+    qbits = f32_to_bf16_bits(rng.standard_normal(c["q_bits"].shape).astype(np.float32) * 2.0)
+    ref_out, ref_lse = oracle_attention(st, O.bf16_to_f64(qbits), c["offsets"])
+    assert np.ptp(ref_lse) > 20.0  # the logits really span a wide range
+    t = step_inputs(st)
+    out, lse = F.ragged_paged_attn(bf16_tensor(qbits, DEV), c["d_offsets"], t.k_cache, t.v_cache,
+                                   t.page_table, t.prefix_len, t.k_blk, t.v_blk, 4, st.sm_scale)
+    torch.cuda.synchronize()
+    T = int(c["offsets"][-1])
+    oerr = np.abs(out[:T].float().cpu().numpy() - ref_out).max()
+    lerr = np.abs(lse[:T].cpu().numpy() - ref_lse).max()
+    # lse grows with the logits: the same relative accuracy as elsewhere
+    assert oerr <= OUT_TOL and lerr <= LSE_TOL * max(1.0, np.abs(ref_lse).max() / 10.0), \
+        (oerr, lerr)
+
+
 def test_attn_poisoned_unused_memory_is_never_read():
     # NaN in every cache slot past a prefix and in spare pages, out-of-range ids past each
     # request's last page: the result must equal the clean run bit for bit
