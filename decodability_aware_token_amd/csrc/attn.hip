@@ -253,60 +253,85 @@ __device__ __forceinline__ void load_q(QOperand<D, QT>& qf, const Cursor& c, con
   }
 }
 
+// Scores of query tile qt: S^T (32 keys x 16 rows) as two 16-key subtiles.
+template <int D, int QT>
+__device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, QT>& qf, int qt,
+                                            int lane, f32x4_t& s0, f32x4_t& s1) {
+  constexpr int NK = D / 32;
+  u32x4_t q[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) q[kk] = qf.get(qt, kk, lane);
+  s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    s0 = mfma_bf16(T.k[0][kk], q[kk], s0);
+    s1 = mfma_bf16(T.k[1][kk], q[kk], s1);
+  }
+}
+
+// One 32-key tile for every query tile of the wave.  Online softmax in the exp2 domain against
+// a reference max per row that moves only when a key's logit exceeds it by more than
+// kRescaleSlack: that test is lane-local (no cross-lane step), and only when some lane finds
+// such a key does the wave take the rows' maxima across lanes and rescale o and l (always on
+// the first tile of a piece, whose reference is -inf).  Otherwise the weights exp2(x - m) stay
+// below 2^kRescaleSlack, which the fp32 sums and bf16 weights hold without loss, and o is
+// touched by the matrix unit only.  The scores of query tile qt+1 are issued before the softmax
+// of tile qt, so the matrix unit works while the vector unit does.
 template <int D, int QT>
 __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
                                              const QOperand<D, QT>& qf,
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
                                              float (&lrun)[QT], float scale_log2, int lane) {
-  constexpr int NK = D / 32, ND = D / 16;
+  constexpr int ND = D / 16;
   const int j4 = lane >> 4;
   // this lane group's 8 keys: slots 0..3 are keys key0 + 4j + (0..3), slots 4..7 are keys
   // key0 + 16 + 4j + (0..3); nv[r] = valid keys of run r
   const int nv[2] = {nvalid - (key0 + 4 * j4), nvalid - (key0 + 16 + 4 * j4)};
-  // Values of keys past the end are zeroed: their weights are zero, but the loaded values may
-  // be anything and 0 * NaN would not vanish.  Branch-free (all-ones masks on full tiles).
-  u32x4_t vmask;
+  const bool full = key0 + 32 <= nvalid;  // wave-uniform: only the last tile of a range is short
+  if (!full) {
+    // Values of keys past the end are zeroed: their weights are zero, but the loaded values
+    // may be anything and 0 * NaN would not vanish.
+    u32x4_t vmask;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int n = nv[w >> 1], b = 2 * (w & 1);
-    vmask[w] = (b + 1 < n) ? 0xffffffffu : ((b < n) ? 0x0000ffffu : 0u);
+    for (int w = 0; w < 4; ++w) {
+      const int n = nv[w >> 1], b = 2 * (w & 1);
+      vmask[w] = (b + 1 < n) ? 0xffffffffu : ((b < n) ? 0x0000ffffu : 0u);
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) T.v[dt] &= vmask;
   }
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) T.v[dt] &= vmask;  // once per tile, in place
+  auto valid = [&](int e) { return full || (e & 3) < nv[e >> 2]; };
+  f32x4_t sc[2][2];
+  tile_scores<D, QT>(T, qf, 0, lane, sc[0][0], sc[0][1]);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    // one query tile at a time: without the barrier the scheduler hoists every tile's operand
-    // reads and keeps them live, which with four tiles no longer fits the registers
+    // with four query tiles, one iteration at a time: otherwise the scheduler hoists every
+    // tile's operand reads and keeps them live, which no longer fits the registers
     if (QT > 2) __builtin_amdgcn_sched_barrier(0);
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const u32x4_t q = qf.get(qt, kk, lane);
-      s0 = mfma_bf16(T.k[0][kk], q, s0);
-      s1 = mfma_bf16(T.k[1][kk], q, s1);
-    }
-    float x[8];
+    const int cur = qt & 1;
+    if (qt + 1 < QT) tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
+    float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = s0[i] * scale_log2;
-      x[4 + i] = s1[i] * scale_log2;
+      s[i] = sc[cur][0][i];
+      s[4 + i] = sc[cur][1][i];
     }
+    // lane-local test against the reference (raw scores: scale_log2 > 0)
+    const float thr = (mrun[qt] + kRescaleSlack) / scale_log2;
+    bool over = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = ((e & 3) < nv[e >> 2]) ? x[e] : -INFINITY;
-    float mx = x[0];
+    for (int e = 0; e < 8; ++e) over = over || (valid(e) && s[e] > thr);
+    if (__ballot(over) != 0) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    // The reference max of a row moves only when the tile's max exceeds it by more than
-    // kRescaleSlack (log2 units): then every row of the query tile is rescaled to its new max
-    // (o, l times exp2(old - new); o is still zero when the old max is -inf).  Otherwise the
-    // weights exp2(x - m) stay below 2^kRescaleSlack, which fp32 sums and bf16 weights hold
-    // without loss, and o needs no multiply: it is then touched by the matrix unit only.
-    if (__ballot(mx > mrun[qt] + kRescaleSlack) != 0) {
+      for (int e = 0; e < 8; ++e)
+        if (valid(e)) mx = fmaxf(mx, s[e] * scale_log2);
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
       const float mnew = fmaxf(mrun[qt], mx);
-      const float alpha = mnew == -INFINITY || mrun[qt] == -INFINITY
-                              ? 0.f : fast_exp2(mrun[qt] - mnew);
+      const float alpha =
+          mnew == -INFINITY || mrun[qt] == -INFINITY ? 0.f : fast_exp2(mrun[qt] - mnew);
       lrun[qt] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) o[qt][dt] *= alpha;
@@ -317,7 +342,8 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pe[e] = fast_exp2(x[e] - msub);
+      pe[e] = fast_exp2(__builtin_fmaf(s[e], scale_log2, -msub));
+      if (!valid(e)) pe[e] = 0.f;
       ls += pe[e];
     }
     lrun[qt] += ls;
