@@ -301,7 +301,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) T.v[dt] &= vmask;
   }
-  auto valid = [&](int e) { return full || (e & 3) < nv[e >> 2]; };
+  const float inv_scale = 1.f / scale_log2;
   f32x4_t sc[2][2];
   tile_scores<D, QT>(T, qf, 0, lane, sc[0][0], sc[0][1]);
 #pragma unroll
@@ -317,16 +317,13 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
       s[i] = sc[cur][0][i];
       s[4 + i] = sc[cur][1][i];
     }
-    // lane-local test against the reference (raw scores: scale_log2 > 0)
-    const float thr = (mrun[qt] + kRescaleSlack) / scale_log2;
-    bool over = false;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) over = over || (valid(e) && s[e] > thr);
-    if (__ballot(over) != 0) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (valid(e)) mx = fmaxf(mx, s[e] * scale_log2);
+    // Lane-local test against the reference on the raw scores (scale_log2 > 0).  Slots past the
+    // end of a short tile hold the score of the last valid key (their keys are clamped to it),
+    // so they need no masking here: they neither raise the row max nor change the test.
+    float smax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    if (__ballot(smax > (mrun[qt] + kRescaleSlack) * inv_scale) != 0) {
+      float mx = smax * scale_log2;
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
       const float mnew = fmaxf(mrun[qt], mx);
@@ -339,13 +336,16 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     }
     const float msub = mrun[qt] == -INFINITY ? 0.f : mrun[qt];
     float pe[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(s[e], scale_log2, -msub));
+    if (!full) {  // slots past the end weigh nothing
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((e & 3) >= nv[e >> 2]) pe[e] = 0.f;
+    }
     float ls = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pe[e] = fast_exp2(__builtin_fmaf(s[e], scale_log2, -msub));
-      if (!valid(e)) pe[e] = 0.f;
-      ls += pe[e];
-    }
+    for (int e = 0; e < 8; ++e) ls += pe[e];
     lrun[qt] += ls;
     u32x4_t pf;
     pf[0] = pack_bf16x2(pe[0], pe[1]);
