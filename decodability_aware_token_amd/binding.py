@@ -203,8 +203,9 @@ def attn_workspace_bytes(B, blk, Hq, Hkv, d, S, max_pages, max_kept) -> int:
 
 def ragged_paged_attn(q, offsets, k_cache, v_cache, page_table, prefix_len, k_blk, v_blk,
                       max_kept: int, sm_scale: float, out=None, lse=None, want_lse=True,
-                      workspace=None):
-    """out [cap, Hq, d] bf16, lse [cap, Hq] f32 (see focus_ragged_paged_attn).
+                      workspace=None, want_out=True):
+    """out [cap, Hq, d] bf16, lse [cap, Hq] f32 (see focus_ragged_paged_attn); want_out=False:
+    log-sum-exp only (out is None; v_cache and v_blk may be None).
 
     q [cap, Hq, d]; k_cache [pages, Hkv, d/8, S, 8]; v_cache [pages, Hkv, S/8, d, 8];
     k_blk [B, Hkv, d/8, blk, 8]; v_blk [B, Hkv, blk/8, d, 8]; page_table [B, max_pages]."""
@@ -214,7 +215,9 @@ def ragged_paged_attn(q, offsets, k_cache, v_cache, page_table, prefix_len, k_bl
     B, max_pages = page_table.shape
     blk = k_blk.shape[3]
     dev = q.device
-    if out is None:
+    if not want_out:
+        out, want_lse = None, True
+    elif out is None:
         out = torch.empty((cap, Hq, d), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((cap, Hq), dtype=torch.float32, device=dev)

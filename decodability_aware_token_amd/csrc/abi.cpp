@@ -280,12 +280,14 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
                             const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
                             int max_kept, float sm_scale, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-  if (!offsets || !prefix_len || !k_blk || !v_blk) return FOCUS_ERR_INVALID_ARG;
-  if (cap > 0 && (!q || !out)) return FOCUS_ERR_INVALID_ARG;
+  // out == NULL: log-sum-exp only (lse required; the values are then not read and may be NULL)
+  const bool lse_only = out == nullptr;
+  if (!offsets || !prefix_len || !k_blk || (!lse_only && !v_blk)) return FOCUS_ERR_INVALID_ARG;
+  if (cap > 0 && (!q || (lse_only && !lse))) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || S <= 0 || cap < 0 ||
       num_pages < 0 || max_pages < 0 || max_kept <= 0)
     return FOCUS_ERR_INVALID_ARG;
-  if (max_pages > 0 && (!k_cache || !v_cache || !page_table || num_pages <= 0))
+  if (max_pages > 0 && (!k_cache || (!lse_only && !v_cache) || !page_table || num_pages <= 0))
     return FOCUS_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return FOCUS_ERR_INVALID_ARG;
   if (Hq % Hkv != 0 || max_kept > blk) return FOCUS_ERR_INVALID_ARG;

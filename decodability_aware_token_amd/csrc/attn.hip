@@ -156,7 +156,7 @@ __device__ __forceinline__ Pages fetch_pages(const Cursor& c, const Params& p,
 // valid key (runs to the last valid run), which lie in allocated pages; keys past the valid
 // length are masked in compute_tile.  An out-of-range page id is replaced by page 0 and
 // reported in T.bad.
-template <int D>
+template <int D, bool WO>
 __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg, const Params& p,
                                           int lane) {
   constexpr int NK = D / 32, ND = D / 16;
@@ -200,6 +200,7 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
     for (int kk = 0; kk < NK; ++kk)
       T.k[s][kk] = load16_stream(kp + ((size_t)((4 * kk) << log2S) << 3));
   }
+  if constexpr (!WO) return;  // log-sum-exp only: no values
   const uint16_t* vp0 = vb[0] + ((size_t)((vrun[0] & (S - 1)) >> 3) * D + m16) * 8 + (vrun[0] & 4);
   const uint16_t* vp1 = vb[1] + ((size_t)((vrun[1] & (S - 1)) >> 3) * D + m16) * 8 + (vrun[1] & 4);
 #pragma unroll
@@ -277,8 +278,9 @@ __device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, 
 // the first tile of a piece, whose reference is -inf).  Otherwise the weights exp2(x - m) stay
 // below 2^kRescaleSlack, which the fp32 sums and bf16 weights hold without loss, and o is
 // touched by the matrix unit only.  The scores of query tile qt+1 are issued before the softmax
-// of tile qt, so the matrix unit works while the vector unit does.
-template <int D, int QT>
+// of tile qt, so the matrix unit works while the vector unit does.  WO = false: log-sum-exp only
+// (no values, no output accumulation).
+template <int D, int QT, bool WO>
 __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
                                              const QOperand<D, QT>& qf,
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
@@ -289,7 +291,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
   // key0 + 16 + 4j + (0..3); nv[r] = valid keys of run r
   const int nv[2] = {nvalid - (key0 + 4 * j4), nvalid - (key0 + 16 + 4 * j4)};
   const bool full = key0 + 32 <= nvalid;  // wave-uniform: only the last tile of a range is short
-  if (!full) {
+  if (WO && !full) {
     // Values of keys past the end are zeroed: their weights are zero, but the loaded values
     // may be anything and 0 * NaN would not vanish.
     u32x4_t vmask;
@@ -330,8 +332,10 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
       const float alpha =
           mnew == -INFINITY || mrun[qt] == -INFINITY ? 0.f : fast_exp2(mrun[qt] - mnew);
       lrun[qt] *= alpha;
+      if constexpr (WO) {
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) o[qt][dt] *= alpha;
+        for (int dt = 0; dt < ND; ++dt) o[qt][dt] *= alpha;
+      }
       mrun[qt] = mnew;
     }
     const float msub = mrun[qt] == -INFINITY ? 0.f : mrun[qt];
@@ -347,6 +351,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
 #pragma unroll
     for (int e = 0; e < 8; ++e) ls += pe[e];
     lrun[qt] += ls;
+    if constexpr (!WO) continue;
     u32x4_t pf;
     pf[0] = pack_bf16x2(pe[0], pe[1]);
     pf[1] = pack_bf16x2(pe[2], pe[3]);
@@ -366,7 +371,7 @@ __device__ __forceinline__ int slice_begin(int i, int total, int n) {
 }
 
 // page_table is a separate restrict argument so that its (uniform) reads become scalar loads.
-template <int D, int QT, int NB>
+template <int D, int QT, int NB, bool WO>
 __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel(
     Params p, const int32_t* __restrict__ page_table) {
   constexpr int NK = D / 32, ND = D / 16, R = 16 * QT;
@@ -518,14 +523,16 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
       const int tok = c.off0 + (rho >> p.log2G);
       if (rho < c.nrows && tok < p.cap) {
         const int h = c.g * p.G + (rho & (p.G - 1));
-        const float inv = nan_out ? __builtin_nanf("") : 1.f / l;
-        uint16_t* orow = p.out + ((size_t)tok * p.Hq + h) * D + 4 * j4;
+        if constexpr (WO) {
+          const float inv = nan_out ? __builtin_nanf("") : 1.f / l;
+          uint16_t* orow = p.out + ((size_t)tok * p.Hq + h) * D + 4 * j4;
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          uint2 w2;
-          w2.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-          w2.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-          *reinterpret_cast<uint2*>(orow + 16 * dt) = w2;
+          for (int dt = 0; dt < ND; ++dt) {
+            uint2 w2;
+            w2.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+            w2.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+            *reinterpret_cast<uint2*>(orow + 16 * dt) = w2;
+          }
         }
         if (j4 == 0 && p.lse != nullptr)
           p.lse[(size_t)tok * p.Hq + h] = nan_out ? __builtin_nanf("") : (m + __log2f(l)) * kLn2;
@@ -560,10 +567,12 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const int row = 16 * qt + m16;
+        if constexpr (WO) {
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[qt][dt]), rs_o,
-                                                 o_off(own_slot, qt, dt), 0, kCpolDevice);
+          for (int dt = 0; dt < ND; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[qt][dt]), rs_o,
+                                                   o_off(own_slot, qt, dt), 0, kCpolDevice);
+        }
         if (j4 == 0) {
           __hip_atomic_store(p.ws_ml + ((size_t)own_slot * 2) * R + row, mrun[qt],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -619,6 +628,7 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
         }
         const float sc = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
         L = __builtin_fmaf(ls, sc, L);
+        if constexpr (WO) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
           const f32x4_t v =
@@ -627,6 +637,7 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
                                                     rs_o, o_off(sl, qt, dt), 0, kCpolDevice));
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[dt][i] = __builtin_fmaf(v[i], sc, acc[dt][i]);
+        }
         }
       }
       write_out(qt, acc, M, L);
@@ -656,7 +667,7 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k) {
     if (k > 0 && tvl + 1 < n) next(L, tvl);
-    load_tile<D>(tl[k], L, fetch_pages(L, p, page_table), p, lane);
+    load_tile<D, WO>(tl[k], L, fetch_pages(L, p, page_table), p, lane);
   }
   if (tvl + 1 < n) next(L, tvl);
   int tv = 0;
@@ -667,12 +678,12 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
   auto step = [&](Tile<D>& X, Tile<D>& Y) {
     const bool live = tv < n;
     if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
-    load_tile<D>(Y, L, fetch_pages(L, p, page_table), p, lane);
+    load_tile<D, WO>(Y, L, fetch_pages(L, p, page_table), p, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     if (live) {
       const int ntp = C.ntp();
       const bool pg = C.tt < ntp;
-      compute_tile<D, QT>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk, qf, o,
+      compute_tile<D, QT, WO>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk, qf, o,
                           mrun, lrun, p.scale_log2, lane);
       bad = bad || X.bad;
       if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
@@ -712,12 +723,12 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int D, int QT>
+template <int D, int QT, bool WO>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
   size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
   if (QT >= 4) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
   constexpr int NB = QT == 1 ? kPrefetchQt1 : 2;
-  hipLaunchKernelGGL((attn_kernel<D, QT, NB>), dim3(plan.wgs), dim3(256), shmem, s, prm,
+  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO>), dim3(plan.wgs), dim3(256), shmem, s, prm,
                      prm.page_table);
   return hipGetLastError();
 }
@@ -781,14 +792,24 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
   prm.ws_o = reinterpret_cast<float*>(ws + plan.cnt_bytes);
   prm.ws_o_bytes = (int)plan.ws_o_bytes;
   prm.ws_ml = reinterpret_cast<float*>(ws + plan.cnt_bytes + plan.ws_o_bytes);
-  if (a.d == 64) {
-    if (plan.qt == 1) return launch_dq<64, 1>(prm, plan, s);
-    if (plan.qt == 2) return launch_dq<64, 2>(prm, plan, s);
-    return launch_dq<64, 4>(prm, plan, s);
+  if (a.out == nullptr) {  // log-sum-exp only
+    if (a.d == 64) {
+      if (plan.qt == 1) return launch_dq<64, 1, false>(prm, plan, s);
+      if (plan.qt == 2) return launch_dq<64, 2, false>(prm, plan, s);
+      return launch_dq<64, 4, false>(prm, plan, s);
+    }
+    if (plan.qt == 1) return launch_dq<128, 1, false>(prm, plan, s);
+    if (plan.qt == 2) return launch_dq<128, 2, false>(prm, plan, s);
+    return launch_dq<128, 4, false>(prm, plan, s);
   }
-  if (plan.qt == 1) return launch_dq<128, 1>(prm, plan, s);
-  if (plan.qt == 2) return launch_dq<128, 2>(prm, plan, s);
-  return launch_dq<128, 4>(prm, plan, s);
+  if (a.d == 64) {
+    if (plan.qt == 1) return launch_dq<64, 1, true>(prm, plan, s);
+    if (plan.qt == 2) return launch_dq<64, 2, true>(prm, plan, s);
+    return launch_dq<64, 4, true>(prm, plan, s);
+  }
+  if (plan.qt == 1) return launch_dq<128, 1, true>(prm, plan, s);
+  if (plan.qt == 2) return launch_dq<128, 2, true>(prm, plan, s);
+  return launch_dq<128, 4, true>(prm, plan, s);
 }
 
 }  // namespace focus

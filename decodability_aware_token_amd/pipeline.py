@@ -194,8 +194,8 @@ class FullDomainScore:
     prefix cache and block keys, and its log-sum-exp output normalises the block keys' weights in
     focus_score_l01_lse.  Project page "FOCUS: DLLMs Know How to Tame Their Compute Bound", card
     "Design" (importance from the early layers' attention).  In a model the two LSEs come with
-    the layers' own attention; here they are computed with the same attention kernel.  V does
-    not enter a log-sum-exp, so both layers' attentions read the one value cache given."""
+    the layers' own attention; here they are computed by the attention kernel's log-sum-exp-only
+    mode, which reads no values."""
 
     def __init__(self, inp: StepInputs, k_cache0: torch.Tensor, k_blk0: torch.Tensor):
         B, blk, Hq, d = inp.q_att.shape
@@ -203,7 +203,6 @@ class FullDomainScore:
         self.inp, self.k_cache0, self.k_blk0 = inp, k_cache0, k_blk0
         self.B, self.blk, self.Hq, self.d = B, blk, Hq, d
         self.offsets = torch.arange(0, (B + 1) * blk, blk, dtype=torch.int32, device=dev)
-        self.out = torch.empty((B * blk, Hq, d), dtype=torch.bfloat16, device=dev)
         self.lse0 = torch.empty((B * blk, Hq), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((B * blk, Hq), dtype=torch.float32, device=dev)
         self.delta = torch.empty((B, blk), dtype=torch.float32, device=dev)
@@ -219,8 +218,8 @@ class FullDomainScore:
         for q, kc, kb, lse in ((i.q0, self.k_cache0, self.k_blk0, self.lse0),
                                (i.q1, i.k_cache, i.k_blk, self.lse1)):
             F.ragged_paged_attn(q.reshape(self.B * self.blk, self.Hq, self.d), self.offsets, kc,
-                                i.v_cache, i.page_table, i.prefix_len, kb, i.v_blk, self.blk,
-                                i.sm_scale, out=self.out, lse=lse, workspace=self.ws_attn)
+                                None, i.page_table, i.prefix_len, kb, None, self.blk,
+                                i.sm_scale, lse=lse, workspace=self.ws_attn, want_out=False)
 
     def score(self):
         i = self.inp

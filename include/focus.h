@@ -204,6 +204,8 @@ int focus_score_select_compact(const void* q0, const void* k0, const void* q1, c
  *   prefix_len [B] i32
  *   q   [cap, Hq, d] bf16 (compacted queries)   out [cap, Hq, d] bf16   lse [cap, Hq] f32 or NULL
  *   (q and out may be NULL when cap == 0: the call then only checks its arguments)
+ *   out == NULL with lse given: log-sum-exp only -- the values are not read (v_cache and v_blk
+ *   may then be NULL), which halves the bytes and the matrix work.
  * max_kept is an upper bound of every kept count (offsets[r+1]-offsets[r]); it sizes the
  * launch.  Rows t >= max_kept of a request are not written.  Rows n >= cap are not read or
  * written.  Device data the host cannot check: a request whose prefix_len is negative or above

@@ -176,7 +176,6 @@ def _attn(**kw):
 
 def test_attn_errors():
     assert _attn(q=None) == F.FOCUS_ERR_INVALID_ARG
-    assert _attn(out=None) == F.FOCUS_ERR_INVALID_ARG
     assert _attn(kc=None) == F.FOCUS_ERR_INVALID_ARG
     assert _attn(pt=None) == F.FOCUS_ERR_INVALID_ARG
     assert _attn(npages=0) == F.FOCUS_ERR_INVALID_ARG
@@ -195,6 +194,10 @@ def test_attn_errors():
     assert need > 0
     assert _attn(maxp=128, ws=None) == F.FOCUS_ERR_WORKSPACE
     assert _attn(maxp=128, wsb=need - 1) == F.FOCUS_ERR_WORKSPACE
+    # log-sum-exp only: no output, no values, but then lse is required
+    assert _attn(out=None, lse=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _attn(out=None, vc=None, vb=None, maxp=128, ws=None) == F.FOCUS_ERR_WORKSPACE
+    assert _attn(vc=None) == F.FOCUS_ERR_INVALID_ARG            # values needed for the output
     # nothing kept: no query or output rows, nothing launched
     assert _attn(cap=0, q=None, out=None) == F.FOCUS_OK
     assert _attn(cap=0, q=None, out=None, S=48) == F.FOCUS_ERR_UNSUPPORTED

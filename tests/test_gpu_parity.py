@@ -372,6 +372,32 @@ def test_attn_output_rounds_to_nearest_even():
     assert np.allclose(lse.cpu().numpy(), np.log(64.0), atol=1e-6)
 
 
+@pytest.mark.parametrize("case", ["g4_d128_s64", "g4_q64rows_blk64", "g8_d128_s16_split",
+                                  "g1_d64_s16"])
+def test_attn_lse_only_equals_full_call(case):
+    # without an output the kernel reads no values (none are given here) and its log-sum-exp
+    # is bit for bit the one of the full call
+    name, over, max_kept = ATTN_CASES[case]
+    over = dict(over)
+    over.setdefault("budget", ("fixed", max_kept))
+    over["score_dtype"] = "bf16"
+    st = make_step(BY_NAME[name].scaled(**over))
+    _announce(f"attn lse only {case}")
+    keep = _random_keep(np.random.default_rng(21), st.B, st.blk, max_kept)
+    c = attn_case_inputs(st, keep)
+    t = step_inputs(st)
+    _, lse_full = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache,
+                                      t.page_table, t.prefix_len, t.k_blk, t.v_blk, max_kept,
+                                      st.sm_scale)
+    out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, None, t.page_table,
+                                   t.prefix_len, t.k_blk, None, max_kept, st.sm_scale,
+                                   want_out=False)
+    torch.cuda.synchronize()
+    T = int(c["offsets"][-1])
+    assert out is None
+    assert np.array_equal(lse[:T].cpu().numpy(), lse_full[:T].cpu().numpy())
+
+
 def test_attn_nothing_kept():
     # every request keeps nothing: zero rows in, zero rows out, and the call succeeds
     _announce("attn nothing kept")
