@@ -298,7 +298,8 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)))
     return FOCUS_ERR_INVALID_ARG;
-  const focus::AttnPlan plan = focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept);
+  const focus::AttnPlan plan =
+      focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept, lse_only);
   if (plan.tiles_bound >= (1LL << 31) || plan.ngroups < 1) return FOCUS_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < plan.ws_bytes) return FOCUS_ERR_WORKSPACE;
   if (cap == 0) return FOCUS_OK;

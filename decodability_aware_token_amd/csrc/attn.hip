@@ -735,23 +735,29 @@ hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
 
 }  // namespace
 
-AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept) {
+AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept,
+                   bool lse_only) {
   AttnPlan pl{};
   const int G = Hq / Hkv;
   const int rows = max_kept * G;
   pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
-  // one 4-wave workgroup per CU (one wave per SIMD, each with NB tiles of 32 keys in flight)
-  pl.wgs = device_cus() * kWgsPerCuQt1;
-  if (pl.qt > 1) pl.wgs = device_cus();
+  // one 4-wave workgroup per CU (one wave per SIMD, each with NB tiles of 32 keys in flight);
+  // without the output the larger query tiles are light enough for two per CU, which hides
+  // their instruction latencies behind each other
+  const int cus = device_cus();
+  pl.wgs = cus * kWgsPerCuQt1;
+  if (pl.qt > 1) pl.wgs = cus * (lse_only ? 2 : 1);
   const long long ntiles_max = ((long long)max_pages * S + 31) / 32 + (blk + 31) / 32;
   pl.tiles_bound = (long long)B * ntiles_max;
   pl.gs = Hkv * pl.nqg;
   pl.ngroups = pl.wgs * kWaves / pl.gs;
   const size_t W = (size_t)pl.wgs * kWaves;
   const size_t R = 16 * (size_t)pl.qt;
-  pl.cnt_bytes = (W * sizeof(int) + 255) & ~(size_t)255;  // arrival counters
-  pl.ws_o_bytes = 2 * W * R * (size_t)d * sizeof(float);
+  // arrival counters sized for the largest grid of either mode, so that the counters of one
+  // workspace never overlap another mode's partials
+  pl.cnt_bytes = ((size_t)2 * cus * kWaves * sizeof(int) + 255) & ~(size_t)255;
+  pl.ws_o_bytes = lse_only ? 0 : 2 * W * R * (size_t)d * sizeof(float);
   pl.ws_ml_bytes = 2 * W * 2 * R * sizeof(float);
   pl.ws_bytes = pl.cnt_bytes + pl.ws_o_bytes + pl.ws_ml_bytes;
   return pl;

@@ -96,7 +96,9 @@ struct AttnPlan {
   size_t ws_ml_bytes;    // their running max / sum
   size_t ws_bytes;       // total workspace
 };
-AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept);
+// lse_only: the plan of the log-sum-exp-only mode (its workspace never exceeds the full one's)
+AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages, int max_kept,
+                   bool lse_only = false);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s);
 
 struct WritebackArgs {

@@ -376,7 +376,9 @@ def test_attn_output_rounds_to_nearest_even():
                                   "g1_d64_s16"])
 def test_attn_lse_only_equals_full_call(case):
     # without an output the kernel reads no values (none are given here) and its log-sum-exp
-    # is bit for bit the one of the full call
+    # is the one of the full call: bit for bit with one query tile per item; with larger query
+    # tiles the mode runs twice the workgroups, so items are cut elsewhere and the merges round
+    # differently (f32 rounding only)
     name, over, max_kept = ATTN_CASES[case]
     over = dict(over)
     over.setdefault("budget", ("fixed", max_kept))
@@ -395,7 +397,11 @@ def test_attn_lse_only_equals_full_call(case):
     torch.cuda.synchronize()
     T = int(c["offsets"][-1])
     assert out is None
-    assert np.array_equal(lse[:T].cpu().numpy(), lse_full[:T].cpu().numpy())
+    a_, b_ = lse[:T].cpu().numpy(), lse_full[:T].cpu().numpy()
+    if max_kept * st.Hq // st.Hkv <= 16:
+        assert np.array_equal(a_, b_)
+    else:
+        assert np.allclose(a_, b_, rtol=0, atol=4e-6 * max(1.0, np.abs(b_).max()))
 
 
 def test_attn_nothing_kept():
