@@ -496,6 +496,54 @@ def test_full_block_step(name, over):
     print(f"rows={st.B * st.blk} out err {oerr:.2e} lse err {lerr:.2e}")
 
 
+def _sample_requests(st, n, seed):
+    rng = np.random.default_rng(seed)
+    sample = set(int(r) for r in rng.choice(st.B, size=min(st.B, n), replace=False))
+    sample.add(int(np.argmax(st.prefix_len)))  # the longest prefix
+    return sorted(sample)
+
+
+def test_full_block_step_full_size_sampled():
+    # the unfocused baseline at the headline size, in the bench's launch configuration (all
+    # 8192 block rows in one call), checked on sampled requests against the oracle
+    from decodability_aware_token_amd import FullBlockStep
+    st = make_step(BY_NAME["sdar_b256_blk32"])
+    _announce(f"full-block step full size B={st.B}")
+    fb = FullBlockStep(step_inputs(st))
+    fb.run()
+    torch.cuda.synchronize()
+    sample = _sample_requests(st, 5, 31)
+    keep = np.ones((st.B, st.blk), dtype=np.uint8)
+    c = attn_case_inputs(st, keep)
+    rows, out, lse = oracle_attention(st, c["q_rows64"], c["offsets"], requests=sample)
+    gidx = torch.as_tensor(rows, device=DEV)
+    oerr = np.abs(fb.out[gidx].float().cpu().numpy() - out).max()
+    lerr = np.abs(fb.lse[gidx].cpu().numpy() - lse).max()
+    assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
+    print(f"sampled {sample}: out err {oerr:.2e} lse err {lerr:.2e}")
+
+
+def test_full_domain_score_full_size_sampled():
+    # full-domain importance at the headline size (both layers' log-sum-exp-only attentions over
+    # all 8192 block rows, then the score), checked on sampled requests against the oracle
+    from decodability_aware_token_amd import FullDomainScore
+    st = make_step(BY_NAME["sdar_b256_blk32"], layer0_prefix=True)
+    _announce(f"full-domain score full size B={st.B}")
+    from workloads.torch_io import upload
+    t = upload(st)
+    fd = FullDomainScore(step_inputs(st), t["k_cache0"], t["k_blk0"])
+    got = fd.run().cpu().numpy()
+    torch.cuda.synchronize()
+    sample = _sample_requests(st, 4, 32)
+    f64 = O.bf16_to_f64
+    ref = O.score_l01_full(f64(st.q0[sample]), f64(st.k0[sample]), f64(st.q1[sample]),
+                           f64(st.k1[sample]), f64(st.k_cache0), f64(st.k_cache),
+                           st.page_table[sample], st.prefix_len[sample], st.sm_scale)
+    err = np.abs(got[sample] - ref).max()
+    assert err <= DELTA_TOL, err
+    print(f"sampled {sample}: delta err {err:.2e}")
+
+
 FULL_DOMAIN_CASES = {"sdar_b32_blk32": {"B": 4}, "longctx_b64_blk32": {"B": 2},
                      "sweep_b128_blk16": {"B": 3}}
 
