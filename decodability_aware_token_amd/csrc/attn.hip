@@ -362,6 +362,18 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
   }
 }
 
+// Workgroup b runs on XCD b mod 8 (round-robin dispatch).  A column group of gs waves spans
+// gs/4 workgroups; they are placed on one XCD (consecutive groups alternate XCDs), which
+// measured ~1-3% faster than groups split across two XCDs.  Identity where the grid does not
+// divide evenly.
+__device__ __forceinline__ int logical_wg(int b, int nwg, int gs) {
+  constexpr int kXcds = 8;
+  const int m = gs / kWaves;  // workgroups per group
+  if (m < 2 || gs % kWaves != 0 || nwg % kXcds != 0 || (nwg / kXcds) % m != 0) return b;
+  const int xcd = b % kXcds, k = b / kXcds;
+  return ((k / m) * kXcds + xcd) * m + k % m;
+}
+
 // Column group whose slice holds column t: the largest i with floor(i*T/n) <= t.
 __device__ __forceinline__ int group_of(int t, int total, int n) {
   return (int)(((long long)(t + 1) * n - 1) / total);
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
 
   // ---- this wave's group, and the group's slice [a, b) of the global column list
   const int total = uni(meta.cum[B]);
-  const int w = blockIdx.x * kWaves + wave;
+  const int w = logical_wg(blockIdx.x, gridDim.x, p.gs) * kWaves + wave;
   const int gi = w / p.gs, hi = w - gi * p.gs;
   const int a = slice_begin(gi, total, p.ngroups);
   const int b = slice_begin(gi + 1, total, p.ngroups);
