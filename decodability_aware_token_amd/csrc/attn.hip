@@ -167,46 +167,55 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
   const int nvalid = paged ? c.plen() : p.blk;
   const int log2S = paged ? p.log2S : p.log2blk;
   const int S = 1 << log2S;
-  const size_t page_elems = (size_t)D << log2S;  // one (page, kv head) block
   const int last = nvalid - 1, last_run = last & ~3;
-  const uint16_t* kb[2];
-  const uint16_t* vb[2];
-  int kkey[2], vrun[2];
+  // Base addresses of the (at most two) (page, kv head) blocks the tile touches, computed once
+  // per tile with wave-uniform (scalar) arithmetic; a lane then picks one of two bases.  A tile
+  // of 32 keys starts at a multiple of 32, so with S >= 32 (and in the block) it lies in one
+  // block: only S = 16 uses the second.
+  const size_t blk_elems = (size_t)D << log2S;  // one (page, kv head) block
+  const uint16_t *k0p, *k1p, *v0p, *v1p;
   bool bad = false;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    kkey[s] = min(key0 + 16 * s + m16, last);
-    vrun[s] = min(key0 + 16 * s + 4 * j4, last_run);
-    if (paged) {
-      const int p0 = key0 >> log2S;
-      int pk = ((kkey[s] >> log2S) == p0) ? pg.a : pg.b;
-      int pv = ((vrun[s] >> log2S) == p0) ? pg.a : pg.b;
-      const bool okk = pk >= 0 && pk < p.num_pages, okv = pv >= 0 && pv < p.num_pages;
-      bad = bad || !okk || !okv;
-      pk = okk ? pk : 0;
-      pv = okv ? pv : 0;
-      kb[s] = p.k_cache + ((size_t)pk * p.Hkv + c.g) * page_elems;
-      vb[s] = p.v_cache + ((size_t)pv * p.Hkv + c.g) * page_elems;
-    } else {
-      kb[s] = p.k_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
-      vb[s] = p.v_blk + ((size_t)c.r * p.Hkv + c.g) * page_elems;
-    }
+  if (paged) {
+    int a = pg.a, b = pg.b;
+    const bool oka = a >= 0 && a < p.num_pages, okb = b >= 0 && b < p.num_pages;
+    bad = !oka || !okb;
+    a = oka ? a : 0;
+    b = okb ? b : 0;
+    const size_t oa = ((size_t)a * p.Hkv + c.g) * blk_elems;
+    const size_t ob = ((size_t)b * p.Hkv + c.g) * blk_elems;
+    k0p = p.k_cache + oa;
+    k1p = p.k_cache + ob;
+    v0p = p.v_cache + oa;
+    v1p = p.v_cache + ob;
+  } else {
+    const size_t o = ((size_t)c.r * p.Hkv + c.g) * blk_elems;
+    k0p = k1p = p.k_blk + o;
+    v0p = v1p = p.v_blk + o;
   }
+  const int p0 = key0 >> log2S;
+  const bool two = paged && S < 32;
   T.bad = bad;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const uint16_t* kp = kb[s] + ((size_t)((j4 << log2S) + (kkey[s] & (S - 1))) << 3);
+    const int kkey = min(key0 + 16 * s + m16, last);
+    const uint16_t* kb = (two && (kkey >> log2S) != p0) ? k1p : k0p;
+    const uint16_t* kp = kb + ((uint32_t)((j4 << log2S) + (kkey & (S - 1))) << 3);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      T.k[s][kk] = load16_stream(kp + ((size_t)((4 * kk) << log2S) << 3));
+      T.k[s][kk] = load16_stream(kp + ((uint32_t)((4 * kk) << log2S) << 3));
   }
   if constexpr (!WO) return;  // log-sum-exp only: no values
-  const uint16_t* vp0 = vb[0] + ((size_t)((vrun[0] & (S - 1)) >> 3) * D + m16) * 8 + (vrun[0] & 4);
-  const uint16_t* vp1 = vb[1] + ((size_t)((vrun[1] & (S - 1)) >> 3) * D + m16) * 8 + (vrun[1] & 4);
+  const uint16_t* vp[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int vrun = min(key0 + 16 * s + 4 * j4, last_run);
+    const uint16_t* vb = (two && (vrun >> log2S) != p0) ? v1p : v0p;
+    vp[s] = vb + ((uint32_t)((vrun & (S - 1)) >> 3) * D + m16) * 8 + (vrun & 4);
+  }
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) {
-    const u32x2_t lo = load8_stream(vp0 + 16 * dt * 8);
-    const u32x2_t hi = load8_stream(vp1 + 16 * dt * 8);
+    const u32x2_t lo = load8_stream(vp[0] + 16 * dt * 8);
+    const u32x2_t hi = load8_stream(vp[1] + 16 * dt * 8);
     T.v[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   }
 }
@@ -277,8 +286,9 @@ __device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, 
 // such a key does the wave take the rows' maxima across lanes and rescale o and l (always on
 // the first tile of a piece, whose reference is -inf).  Otherwise the weights exp2(x - m) stay
 // below 2^kRescaleSlack, which the fp32 sums and bf16 weights hold without loss, and o is
-// touched by the matrix unit only.  The scores of query tile qt+1 are issued before the softmax
-// of tile qt, so the matrix unit works while the vector unit does.  WO = false: log-sum-exp only
+// touched by the matrix unit only.  With up to two query tiles the scores of tile qt+1 are issued
+// before the softmax of tile qt, so the matrix unit works while the vector unit does.  WO = false:
+// log-sum-exp only
 // (no values, no output accumulation).
 template <int D, int QT, bool WO>
 __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
@@ -312,7 +322,11 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     // tile's operand reads and keeps them live, which no longer fits the registers
     if (QT > 2) __builtin_amdgcn_sched_barrier(0);
     const int cur = qt & 1;
-    if (qt + 1 < QT) tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
+    // up to two query tiles: the next tile's scores are issued ahead; with four the extra
+    // registers would spill, so each tile's scores are computed at its turn
+    if (QT < 4 && qt + 1 < QT)
+      tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
+    if (QT >= 4 && qt > 0) tile_scores<D, QT>(T, qf, qt, lane, sc[cur][0], sc[cur][1]);
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
