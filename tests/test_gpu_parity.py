@@ -747,10 +747,13 @@ def test_score_select_compact_equals_two_calls(name, over, cap_frac):
     torch.cuda.synchronize()
     T = min(int(o1[-1]), cap)
     # the launch bound max_kept changes how many workgroups gather, never the results (even when
-    # the budgets exceed it)
-    for mk in (1, 3, st.blk):
+    # the budgets exceed it); repeated calls may share one workspace
+    ws = torch.zeros(F.lib().focus_score_l01_workspace_size(st.B, st.blk, st.Hq, st.Hkv, st.d),
+                     dtype=torch.uint8, device="cuda")
+    for mk in (1, 1, 3, st.blk, 2):
         d2, k2, c2, o2, p2, g2 = F.score_select_compact(t.q0, t.k0, t.q1, t.k1, t.sm_scale,
-                                                        t.masked, budget, sets, cap, max_kept=mk)
+                                                        t.masked, budget, sets, cap, max_kept=mk,
+                                                        workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(d1, d2) and torch.equal(k1, k2) and torch.equal(c1, c2)
         assert torch.equal(o1, o2)
@@ -760,3 +763,41 @@ def test_score_select_compact_equals_two_calls(name, over, cap_frac):
     # the kept counts follow the budgets: min(max(b, 0), masked count)
     m = t.masked.ne(0).sum(1).to(torch.int32)
     assert torch.equal(c2, torch.minimum(budget.clamp(min=0), m))
+
+
+def test_score_select_compact_workspace_shared_across_shapes():
+    # one workspace serves repeated calls of two shapes with a scoring call of a third shape in
+    # between
+    cases = [make_step(BY_NAME["sdar_b32_blk32"].scaled(B=300, prefix=("fixed", 64),
+                                                        max_prefix=64)),
+             make_step(BY_NAME["sweep_b128_blk16"].scaled(B=260, prefix=("fixed", 64),
+                                                          max_prefix=64))]
+    other_st = make_step(BY_NAME["sweep_b128_blk64"].scaled(B=9, prefix=("fixed", 64),
+                                                            max_prefix=64))
+    other = step_inputs(other_st)
+    _announce("score_select_compact shared workspace")
+    size = max(F.lib().focus_score_l01_workspace_size(c.B, c.blk, c.Hq, c.Hkv, c.d)
+               for c in cases + [other_st])
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    refs = []
+    for st in cases:
+        t = step_inputs(st)
+        rng = np.random.default_rng(st.B)
+        budget = torch.from_numpy(rng.integers(0, st.blk + 1, size=st.B).astype(np.int32)).cuda()
+        sets = [t.q_att] if t.hidden is None else [t.hidden, t.q_att]
+        cap = st.B * st.blk
+        d1, k1, c1 = F.score_select(t.q0, t.k0, t.q1, t.k1, t.sm_scale, t.masked, budget)
+        o1, p1, g1 = F.compact_multi(k1, sets, cap)
+        refs.append((t, budget, sets, cap, (d1, k1, c1, o1, p1, g1)))
+    for rnd in range(2):
+        for t, budget, sets, cap, ref in refs:
+            got = F.score_select_compact(t.q0, t.k0, t.q1, t.k1, t.sm_scale, t.masked, budget,
+                                         sets, cap, max_kept=1, workspace=ws)
+            F.score_l01(other.q0, other.k0, other.q1, other.k1, other.sm_scale, workspace=ws)
+            torch.cuda.synchronize()
+            T = int(ref[3][-1])  # rows kept (below cap): the rest of the outputs is not written
+            for x, y in zip(ref[:4], got[:4]):
+                assert torch.equal(x, y), rnd
+            assert torch.equal(ref[4][:T], got[4][:T]), rnd
+            for x, y in zip(ref[5], got[5]):
+                assert torch.equal(x[:T].view(torch.int16), y[:T].view(torch.int16)), rnd
