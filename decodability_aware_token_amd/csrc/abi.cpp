@@ -262,7 +262,8 @@ int focus_score_select_compact(const void* q0, const void* k0, const void* q1, c
   int64_t bytes = 0;
   for (int si = 0; si < nsets; ++si) bytes += row_bytes[si];
   const int64_t per_wg = 256 * 8 * 16;
-  a.nsplit = (int)std::min<int64_t>(16, std::max<int64_t>(1, (max_kept * bytes + per_wg - 1) / per_wg));
+  a.nsplit = (int)std::min<int64_t>(
+      16, std::max<int64_t>(1, (max_kept * bytes + per_wg - 1) / per_wg));
   return status_of(focus::launch_select_compact(a, stream));
 }
 

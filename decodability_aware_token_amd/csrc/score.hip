@@ -3,15 +3,16 @@
 // block's keys).  Project page "FOCUS: DLLMs Know How to Tame Their Compute Bound", Overview
 // cards "Design" and "Decodability Signal"; the paper's abstract (attention-derived importance).
 //
-// One workgroup per (request r, kv head g), 4 waves.  For each layer
-// the K tile of kv head g and the Q tiles of GS of its query heads are staged in LDS with
-// coalesced 16-byte loads, all issued before the LDS writes, with the next pass in flight.  A wave takes one (query head, 16-query tile) unit at a time and
-// computes S^T = K Q^T (keys x queries) on MFMA, so a lane holds one query's scores for 4 keys
-// of each 16-key tile: the row softmax over keys needs a local reduction plus two cross-lane
-// steps, and the column sums accumulate in registers across units and both layers (layer 0
-// subtracts, layer 1 adds).  The 16 query lanes are summed once at the end, the 4 waves in LDS
-// in a fixed order.  A second small kernel sums each request's Hkv partials in kv-head order
-// (deterministic, no atomics) and can run the request's selection right away.
+// One workgroup per (request r, kv head g), 4 waves.  For each layer the K tile of kv head g
+// and the Q tiles of GS of its query heads are staged in LDS with coalesced 16-byte loads, all
+// issued before the LDS writes, with the next pass in flight.  A wave takes one (query head,
+// 16-query tile) unit at a time and computes S^T = K Q^T (keys x queries) on MFMA, so a lane
+// holds one query's scores for 4 keys of each 16-key tile: the row softmax over keys needs a
+// local reduction plus two cross-lane steps, and the column sums accumulate in registers across
+// units and both layers (layer 0 subtracts, layer 1 adds).  The 16 query lanes are summed once
+// at the end, the 4 waves in LDS in a fixed order.  A second small kernel sums each request's
+// Hkv partials in kv-head order (deterministic, no atomics) and can run the request's selection
+// right away.
 #include "device_common.h"
 #include "launch.h"
 #include "select_impl.h"
