@@ -332,8 +332,8 @@ def main():
                          "to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md "
-              "for how the step would shard by request).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (the step would shard "
+              "by request, each GPU running the whole step on its share).", file=sys.stderr)
         sys.exit(2)
 
     if args.summarize_profiles:

@@ -1,0 +1,91 @@
+"""Host logic of bench.py (no GPU): the one-GPU contract, the algorithmic byte and flop counts
+the roofline divides by, and the profile summaries' counter scaling."""
+import csv
+import json
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_attention_algorithmic_counts_by_hand():
+    # request 0: prefix 70, two kept tokens; request 1: nothing kept (moves nothing)
+    st = types.SimpleNamespace(prefix_len=np.array([70, 5]), blk=32, Hkv=2, d=64, Hq=4, S=64)
+    by, fl = bench.attn_algorithmic(st, np.array([2, 0]))
+    kv = (70 + 32) * 2 * 64 * 2 * 2          # prefix + block K and V, bf16
+    qo = 2 * 4 * 64 * 2 * 2                  # kept queries and outputs
+    lse = 2 * 4 * 4
+    table = 4 * 2 + 8                        # two page ids, prefix length and offset
+    assert by == kv + qo + lse + table
+    assert fl == 4 * 2 * 4 * (70 + 32) * 64
+
+
+def test_score_algorithmic_counts_by_hand():
+    st = types.SimpleNamespace(B=3, blk=16, Hq=4, Hkv=2, d=64, score_dtype="bf16")
+    by, fl = bench.score_algorithmic(st)
+    assert by == 2 * 3 * 16 * (4 + 2) * 64 * 2 + 4 * 3 * 16
+    assert fl == 2 * 2 * 3 * 16 * 16 * 4 * 64
+    st.score_dtype = "f32"
+    assert bench.score_algorithmic(st)[0] == 2 * 3 * 16 * (4 + 2) * 64 * 4 + 4 * 3 * 16
+
+
+def _write_pmc(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, value) in enumerate(rows):
+            w.writerow([i, name, counter, value])
+
+
+def test_profile_summary_scales_counters_by_the_copy(tmp_path, monkeypatch):
+    out = tmp_path / "out"
+    attn = "void focus::(anonymous namespace)::attn_kernel<128, 1, 2, true>(focus::Params)"
+    copy = "__amd_rocclr_copyBuffer(void*)"
+    # the copy of 1 GiB reads as half its bytes in FETCH_SIZE and all of them in WRITE_SIZE
+    _write_pmc(out / "pmc" / "copy_fetch", "FETCH_SIZE", [(copy, 524288.0), (copy, 12.0)])
+    _write_pmc(out / "pmc" / "copy_write", "WRITE_SIZE", [(copy, 1048576.0)])
+    _write_pmc(out / "pmc" / "step_fetch", "FETCH_SIZE",
+               [(attn, 1000.0), (attn, 3000.0), (attn, 2000.0)])      # median 2000 KiB
+    _write_pmc(out / "pmc" / "step_write", "WRITE_SIZE", [(attn, 10.0)])
+    os.makedirs(out / "prof")
+    with open(out / "prof" / "trace_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writerow([attn, 3, 150000, 140000, 160000, 80.0])
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
+    bench.summarize_profiles(str(out), "w")
+    rec = json.load(open(tmp_path / "profiles" / "attn_traffic_w.json"))
+    assert rec["kernel"] == "attn_kernel<128, 1, 2, true>"
+    assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
+    assert rec["hbm_read_bytes"] == 2000 * 1024 * 2
+    assert rec["hbm_write_bytes"] == 10 * 1024
+    table = open(tmp_path / "profiles" / "kernels_w.txt").read()
+    assert "attn_kernel<128, 1, 2, true>" in table and "150.00" in table
+
+
+def test_counter_traffic_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
+    os.makedirs(tmp_path / "profiles")
+    with open(tmp_path / "profiles" / "attn_traffic_w.json", "w") as fh:
+        json.dump({"kernel_source_hash": "abc", "hbm_bytes_per_launch": 123}, fh)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    assert bench.counter_traffic("w") == 123
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
+    assert bench.counter_traffic("w") is None
+    assert bench.counter_traffic("other") is None
