@@ -481,7 +481,18 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
   if (gi >= p.ngroups || a >= b) return;
 
   // largest r with cum[r] <= col (requests without columns are skipped by the search)
+  // (cum is non-decreasing, so each ballot below is a prefix of the lanes: two LDS reads per
+  // lane instead of a chain of log2(B) dependent ones)
   auto locate = [&](int col) {
+    const int s = (B + 63) >> 6;  // requests per lane in the first round
+    if (s <= 64) {
+      const int i1 = lane * s;
+      const uint64_t m1 = __ballot(i1 < B && meta.cum[min(i1, B - 1)] <= col);
+      const int base = (__popcll(m1) - 1) * s;  // lane 0 always holds: cum[0] = 0 <= col
+      const int i2 = base + lane;
+      const uint64_t m2 = __ballot(lane < s && i2 < B && meta.cum[min(i2, B - 1)] <= col);
+      return uni(base + __popcll(m2) - 1);
+    }
     int lo = 0, hi_r = B;
     while (hi_r - lo > 1) {
       const int mid = (lo + hi_r) >> 1;
