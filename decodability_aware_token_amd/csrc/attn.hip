@@ -56,6 +56,8 @@ constexpr int kRawBufferFormat = 0x00020000;
 // how far (log2 units) a row's logits may exceed its reference max before the running output
 // is rescaled: softmax weights stay below 2^8
 constexpr float kRescaleSlack = 8.f;
+// pieces of a cut item merged with all their loads in flight together (more go one by one)
+constexpr int kMaxMerge = 8;
 
 struct Params {
   const uint16_t* q;
@@ -627,7 +629,90 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
     }
     if (!last) return;
     // last arrival: merge every piece in key order (own piece from registers), then reset the
-    // counter for the next call
+    // counter for the next call.  The same operations whether a piece comes from registers or
+    // from memory, so the result does not depend on which piece arrived last.  Up to
+    // kMaxMerge pieces, their slots are found once, every piece's max and sum loads are issued
+    // together, and piece k+1's partial O is loaded while piece k is accumulated (no chain of
+    // dependent round trips); items cut into more pieces take them one by one.
+    // (32-row tiles only: the 16-row kernel is held to 256 registers and its items are long,
+    // and the 64-row kernels are short of registers; those merge piece by piece)
+    constexpr int MM = kMaxMerge;
+    if (QT == 2 && npieces <= MM) {
+      int slot[MM];
+      {
+        int tp = c.start;
+#pragma unroll
+        for (int k = 0; k < MM; ++k) {
+          slot[k] = own_slot;
+          if (k < npieces) {
+            const int gv = group_of(tp, total, p.ngroups);
+            slot[k] = tp == c.start ? 2 * (gv * p.gs + hi) + 1 : 2 * (gv * p.gs + hi);
+            tp = slice_begin(gv + 1, total, p.ngroups);
+          }
+        }
+      }
+      auto fetch_o = [&](int sl, int qt, f32x4_t (&dst)[ND]) {
+        if (sl == own_slot) return;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+          dst[dt] = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_o, o_off(sl, qt, dt), 0,
+                                                             kCpolDevice));
+      };
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int row = 16 * qt + m16;
+        float ms[MM], ls[MM];
+#pragma unroll
+        for (int k = 0; k < MM; ++k) {
+          ms[k] = -INFINITY;
+          ls[k] = 0.f;
+          if (k < npieces) {
+            if (slot[k] == own_slot) {
+              ms[k] = mrun[qt];
+              ls[k] = nan_out ? __builtin_nanf("") : lt[qt];
+            } else {
+              ms[k] = __hip_atomic_load(p.ws_ml + ((size_t)slot[k] * 2) * R + row,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              ls[k] = __hip_atomic_load(p.ws_ml + ((size_t)slot[k] * 2 + 1) * R + row,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+        f32x4_t ob[2][ND];
+        if constexpr (WO) fetch_o(slot[0], qt, ob[0]);
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < MM; ++k)
+          if (k < npieces) M = fmaxf(M, ms[k]);
+        float L = 0.f;
+        f32x4_t acc[ND];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < MM; ++k) {
+          if (k < npieces) {
+            if constexpr (WO) {
+              if (k + 1 < npieces) fetch_o(slot[k + 1], qt, ob[(k + 1) & 1]);
+            }
+            const float sc = ms[k] == -INFINITY ? 0.f : fast_exp2(ms[k] - M);
+            L = __builtin_fmaf(ls[k], sc, L);
+            if constexpr (WO) {
+              const bool own = slot[k] == own_slot;
+#pragma unroll
+              for (int dt = 0; dt < ND; ++dt) {
+                const f32x4_t v = own ? o[qt][dt] : ob[k & 1][dt];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[dt][i] = __builtin_fmaf(v[i], sc, acc[dt][i]);
+              }
+            }
+          }
+        }
+        write_out(qt, acc, M, L);
+      }
+      if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const int row = 16 * qt + m16;
