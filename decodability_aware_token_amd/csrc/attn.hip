@@ -267,14 +267,12 @@ __device__ __forceinline__ void load_q(QOperand<D, QT>& qf, const Cursor& c, con
   }
 }
 
-// Scores of query tile qt: S^T (32 keys x 16 rows) as two 16-key subtiles.
-template <int D, int QT>
-__device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, QT>& qf, int qt,
-                                            int lane, f32x4_t& s0, f32x4_t& s1) {
+// Scores of one query tile from its Q^T fragments: S^T (32 keys x 16 rows) as two 16-key
+// subtiles.
+template <int D>
+__device__ __forceinline__ void tile_scores_q(const Tile<D>& T, const u32x4_t (&q)[D / 32],
+                                              f32x4_t& s0, f32x4_t& s1) {
   constexpr int NK = D / 32;
-  u32x4_t q[NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) q[kk] = qf.get(qt, kk, lane);
   s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -282,6 +280,17 @@ __device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, 
     s0 = mfma_bf16(T.k[0][kk], q[kk], s0);
     s1 = mfma_bf16(T.k[1][kk], q[kk], s1);
   }
+}
+
+// Scores of query tile qt.
+template <int D, int QT>
+__device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, QT>& qf, int qt,
+                                            int lane, f32x4_t& s0, f32x4_t& s1) {
+  constexpr int NK = D / 32;
+  u32x4_t q[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) q[kk] = qf.get(qt, kk, lane);
+  tile_scores_q<D>(T, q, s0, s1);
 }
 
 // One 32-key tile for every query tile of the wave.  Online softmax in the exp2 domain against
@@ -319,7 +328,19 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
   }
   const float inv_scale = 1.f / scale_log2;
   f32x4_t sc[2][2];
-  tile_scores<D, QT>(T, qf, 0, lane, sc[0][0], sc[0][1]);
+  // four query tiles without the output (registers to spare): the next query tile's Q^T
+  // fragments are read from LDS one iteration ahead, so the score products do not wait for
+  // LDS (with the output the extra registers cost more than the waits)
+  constexpr int NK = D / 32;
+  constexpr bool kQAhead = QT >= 4 && !WO;
+  u32x4_t qfr[2][NK];  // fragments of the query tiles of parity 0 and 1
+  if constexpr (kQAhead) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qfr[0][kk] = qf.get(0, kk, lane);
+    tile_scores_q<D>(T, qfr[0], sc[0][0], sc[0][1]);
+  } else {
+    tile_scores<D, QT>(T, qf, 0, lane, sc[0][0], sc[0][1]);
+  }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     // with four query tiles, one iteration at a time: otherwise the scheduler hoists every
@@ -330,7 +351,15 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     // registers would spill, so each tile's scores are computed at its turn
     if (QT < 4 && qt + 1 < QT)
       tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
-    if (QT >= 4 && qt > 0) tile_scores<D, QT>(T, qf, qt, lane, sc[cur][0], sc[cur][1]);
+    if constexpr (kQAhead) {
+      if (qt > 0) tile_scores_q<D>(T, qfr[cur], sc[cur][0], sc[cur][1]);
+      if (qt + 1 < QT) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) qfr[cur ^ 1][kk] = qf.get(qt + 1, kk, lane);
+      }
+    } else if (QT >= 4 && qt > 0) {
+      tile_scores<D, QT>(T, qf, qt, lane, sc[cur][0], sc[cur][1]);
+    }
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
