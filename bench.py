@@ -326,7 +326,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--summarize-profiles", metavar="OUT_ROOT",
                     help="write the profiles/ summaries from the CSV output of the rocprofv3 "
-                         "commands in PROFILE_CMDS (run with OUT_ROOT as their gpurun_out)")
+                         "commands in PROFILE_CMDS (OUT_ROOT is the folder that holds their -d output)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes) 5 times, "
                          "to scale HBM byte counters")
