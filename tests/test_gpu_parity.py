@@ -178,6 +178,10 @@ ATTN_CASES = {
                                                 "prefix": ("uniform", 3000, 5000),
                                                 "max_prefix": 5000}, 2),
     "g4_long_split": ("longctx_b64_blk32", {"B": 4}, 4),
+    # two long requests with 32 and 64 rows per item: each item is cut into more pieces than
+    # the 32-row kernel merges in one batch, so the piece-by-piece merge runs as well
+    "g4_q32rows_many_pieces": ("longctx_b64_blk32", {"B": 2}, 8),
+    "g4_q64rows_many_pieces": ("longctx_b64_blk32", {"B": 2}, 16),
 }
 
 
@@ -373,7 +377,7 @@ def test_attn_output_rounds_to_nearest_even():
 
 
 @pytest.mark.parametrize("case", ["g4_d128_s64", "g4_q64rows_blk64", "g8_d128_s16_split",
-                                  "g1_d64_s16"])
+                                  "g1_d64_s16", "g4_q64rows_many_pieces"])
 def test_attn_lse_only_equals_full_call(case):
     # without an output the kernel reads no values (none are given here) and its log-sum-exp
     # is the one of the full call: bit for bit with one query tile per item; with larger query
