@@ -303,12 +303,18 @@ __device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, 
 // before the softmax of tile qt, so the matrix unit works while the vector unit does.  WO = false:
 // log-sum-exp only
 // (no values, no output accumulation).
+// nq (wave-uniform): query tiles of this item's query group that hold rows.  With four query
+// tiles per wave the others are padding and are skipped (their m, l and O stay at the initial
+// -inf, 0, 0, are never written out and weigh zero in a merge), and a group without rows
+// computes nothing: 16-token blocks, whose items mostly fill one of the four tiles, 171 -> 153
+// us.  With two the check measured slower (the pair's scores are issued together).
 template <int D, int QT, bool WO>
-__device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
+__device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, int nq,
                                              const QOperand<D, QT>& qf,
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
                                              float (&lrun)[QT], float scale_log2, int lane) {
   constexpr int ND = D / 16;
+  if (QT > 2 && nq <= 0) return;
   const int j4 = lane >> 4;
   // this lane group's 8 keys: slots 0..3 are keys key0 + 4j + (0..3), slots 4..7 are keys
   // key0 + 16 + 4j + (0..3); nv[r] = valid keys of run r
@@ -346,6 +352,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
     // with four query tiles, one iteration at a time: otherwise the scheduler hoists every
     // tile's operand reads and keeps them live, which no longer fits the registers
     if (QT > 2) __builtin_amdgcn_sched_barrier(0);
+    if (QT > 2 && qt > 0 && qt >= nq) break;
     const int cur = qt & 1;
     // up to two query tiles: the next tile's scores are issued ahead; with four the extra
     // registers would spill, so each tile's scores are computed at its turn
@@ -353,7 +360,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid,
       tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
     if constexpr (kQAhead) {
       if (qt > 0) tile_scores_q<D>(T, qfr[cur], sc[cur][0], sc[cur][1]);
-      if (qt + 1 < QT) {
+      if (qt + 1 < QT && qt + 1 < nq) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) qfr[cur ^ 1][kk] = qf.get(qt + 1, kk, lane);
       }
@@ -836,8 +843,9 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
     if (live) {
       const int ntp = C.ntp();
       const bool pg = C.tt < ntp;
-      compute_tile<D, QT, WO>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk, qf, o,
-                          mrun, lrun, p.scale_log2, lane);
+      const int nq = (C.nrows - C.qg * R + 15) >> 4;
+      compute_tile<D, QT, WO>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk, nq,
+                              qf, o, mrun, lrun, p.scale_log2, lane);
       bad = bad || X.bad;
       if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
         finalize(C, bad);
