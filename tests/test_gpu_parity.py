@@ -182,25 +182,30 @@ ATTN_CASES = {
     # the 32-row kernel merges in one batch, so the piece-by-piece merge runs as well
     "g4_q32rows_many_pieces": ("longctx_b64_blk32", {"B": 2}, 8),
     "g4_q64rows_many_pieces": ("longctx_b64_blk32", {"B": 2}, 16),
+    # launch bound above every request's kept count (as with adaptive budgets): four 64-row
+    # query groups per kv head, of which two, or one, hold rows (the others compute nothing)
+    "g4_q64rows_bound_2_of_4_groups": ("sweep_b128_blk64", {"B": 6}, 20, 64),
+    "g4_q64rows_bound_1_of_4_groups": ("sweep_b128_blk64", {"B": 6}, 12, 64),
 }
 
 
 @pytest.mark.parametrize("case", list(ATTN_CASES))
 def test_attn_isolated(case):
-    name, over, max_kept = ATTN_CASES[case]
+    name, over, max_kept = ATTN_CASES[case][:3]
+    bound = ATTN_CASES[case][3] if len(ATTN_CASES[case]) > 3 else max_kept
     over = dict(over)
     over.setdefault("budget", ("fixed", max_kept))
     over["score_dtype"] = "bf16"
     st = make_step(BY_NAME[name].scaled(**over))
     _announce(f"attn {case} B={st.B} G={st.Hq // st.Hkv} d={st.d} S={st.S} blk={st.blk} "
-              f"max_kept={max_kept} prefix_max={int(st.prefix_len.max())}")
+              f"max_kept={max_kept} bound={bound} prefix_max={int(st.prefix_len.max())}")
     rng = np.random.default_rng(zlib.crc32(case.encode()) % 1000)
     keep = _random_keep(rng, st.B, st.blk, max_kept)
     c = attn_case_inputs(st, keep)
     ref_out, ref_lse = oracle_attention(st, c["q_rows64"], c["offsets"])
     t = step_inputs(st)
     out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache, t.page_table,
-                                   t.prefix_len, t.k_blk, t.v_blk, max_kept, st.sm_scale)
+                                   t.prefix_len, t.k_blk, t.v_blk, bound, st.sm_scale)
     torch.cuda.synchronize()
     T = int(c["offsets"][-1])
     go = out[:T].float().cpu().numpy()
