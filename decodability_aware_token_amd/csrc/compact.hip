@@ -199,8 +199,17 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectCompactArgs a
 
   // 2. delta of position lane (fixed head order), then the selection
   const float* pr = a.part + (size_t)r * a.Hkv * BLK + min(lane, BLK - 1);
+  // eight partials loaded before any is added (a loop adding each as it arrives waits for every
+  // load in turn), then summed in head order
   float dj = 0.f;
-  for (int g = 0; g < a.Hkv; ++g) dj += pr[(size_t)g * BLK];
+  for (int g0 = 0; g0 < a.Hkv; g0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pr[(size_t)min(g0 + u, a.Hkv - 1) * BLK];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (g0 + u < a.Hkv) dj += v[u];
+  }
   if (lane >= BLK) dj = 0.f;
   const Selection sel = select_compute(sl, r, dj, lane);
   const bool kj = sel.kept;

@@ -236,7 +236,16 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(const float* __restri
   float sum = 0.f;
   if (lane < blk) {
     const float* pr = part + (size_t)r * Hkv * blk + lane;
-    for (int g = 0; g < Hkv; ++g) sum += pr[(size_t)g * blk];
+    // eight partials loaded before any is added (a loop adding each as it arrives waits for
+    // every load in turn), then summed in head order
+    for (int g0 = 0; g0 < Hkv; g0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pr[(size_t)min(g0 + u, Hkv - 1) * blk];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (g0 + u < Hkv) sum += v[u];
+    }
     delta[(size_t)r * blk + lane] = sum;
   }
   if (fuse_select) select_request(sel, r, sum, lane);
