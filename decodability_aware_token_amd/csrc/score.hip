@@ -188,21 +188,33 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
     if (pi > 0) __syncthreads();  // every wave is done with the previous pass's tiles
     store_pass<T, BLK, D, GS>(ps, Ks, Qs, tid);
     __syncthreads();
+    const int layer = pi / groups, h0 = (pi % groups) * GS;
+    const float sign = layer ? 1.f : -1.f;
+    // this wave's units of the pass: u = wave + 4k.  Full domain: their rows' log-sum-exps are
+    // loaded before the next pass's tiles, since loads complete in issue order and a wait for
+    // one issued after the prefetch would wait for the whole prefetch
+    constexpr int NU = GS * NMT, UPW = (NU + 3) / 4;
+    float row_lse_log2[UPW];
+#pragma unroll
+    for (int k = 0; k < UPW; ++k) {
+      row_lse_log2[k] = 0.f;
+      if constexpr (FULL) {
+        const int u = min(wave + 4 * k, NU - 1), hh = u / NMT, nt = u % NMT;
+        const float* lse = layer ? lse1 : lse0;  // [B, BLK, Hq], natural log
+        row_lse_log2[k] = lse[((size_t)r * BLK + 16 * nt + n16) * Hq + g * G + h0 + hh];
+      }
+    }
     if (pi + 1 < npass) {
       const int nl = (pi + 1) / groups, nh = ((pi + 1) % groups) * GS;
       load_pass<T, BLK, D, GS>(ps, nl ? q1 : q0, nl ? k1 : k0, r, g, Hq, Hkv, G, nh, tid);
     }
-    const int layer = pi / groups, h0 = (pi % groups) * GS;
-    const float sign = layer ? 1.f : -1.f;
-    for (int u = wave; u < GS * NMT; u += 4) {
+#pragma unroll
+    for (int k = 0; k < UPW; ++k) {
+      const int u = wave + 4 * k;
+      if (u >= NU) break;
       const int hh = u / NMT, nt = u % NMT;
-      float row_lse_log2 = 0.f;
-      if constexpr (FULL) {
-        const float* lse = layer ? lse1 : lse0;  // [B, BLK, Hq], natural log
-        row_lse_log2 = lse[((size_t)r * BLK + 16 * nt + n16) * Hq + g * G + h0 + hh] * kLog2e;
-      }
-      score_unit<T, BLK, D, GS, FULL>(Ks, Qs, hh, nt, n16, j4, scale_log2, sign, row_lse_log2,
-                                      colacc);
+      score_unit<T, BLK, D, GS, FULL>(Ks, Qs, hh, nt, n16, j4, scale_log2, sign,
+                                      row_lse_log2[k] * kLog2e, colacc);
     }
   }
 
