@@ -175,6 +175,8 @@ def select_budget(delta: np.ndarray, masked: np.ndarray, budget: Optional[np.nda
     [PP header]: non-decodable tokens are evicted.  Readings: a larger delta means more likely
     decodable; only masked tokens are candidates (decoded ones are never kept);
     k_r = min(max(b_r, 0), m_r); equal scores are ordered by block position, lower first.
+    A score that is not a number ranks as minus infinity (the pages never meet one; this keeps
+    the order total, so exactly k_r tokens are kept).
     Returns keep [B, blk] uint8 and kept_count [B] int32.
     """
     B, blk = delta.shape
@@ -184,16 +186,25 @@ def select_budget(delta: np.ndarray, masked: np.ndarray, budget: Optional[np.nda
         cand = [j for j in range(blk) if masked[r, j]]
         b = request_budget(delta[r], masked[r], None if budget is None else budget[r], rule)
         k = min(max(b, 0), len(cand))
-        order = sorted(cand, key=lambda j: (-float(delta[r, j]), j))
+        order = sorted(cand, key=lambda j: (-rank_key(delta[r, j]), j))
         for j in order[:k]:
             keep[r, j] = 1
         kept[r] = k
     return keep, kept
 
 
+def rank_key(x) -> float:
+    """The value a score is ranked by: itself, or minus infinity if it is not a number."""
+    x = float(x)
+    return -math.inf if math.isnan(x) else x
+
+
 def kth_boundary(delta_r: np.ndarray, masked_r: np.ndarray, k: int) -> float:
-    """The k-th largest masked score of a request (nan if k == 0): the selection boundary."""
-    cand = sorted((float(delta_r[j]) for j in range(len(delta_r)) if masked_r[j]), reverse=True)
+    """The k-th largest masked score of a request (its rank key), clipped to the last
+    candidate when k exceeds their number; nan if k <= 0 or nothing is masked.  This is the
+    selection boundary: the smallest kept score."""
+    cand = sorted((rank_key(delta_r[j]) for j in range(len(delta_r)) if masked_r[j]),
+                  reverse=True)
     if k <= 0 or not cand:
         return float("nan")
     return cand[min(k, len(cand)) - 1]

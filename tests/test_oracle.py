@@ -221,7 +221,83 @@ def test_full_domain_score_is_layer_difference_with_own_caches():
     assert abs(a.sum()) > 1e-6
 
 
+def test_full_domain_score_orientation_closed_form():
+    # Layer 0: Q == 0, so each block query spreads its weight evenly over all P + blk keys of
+    # that layer (prefix and block): I0(j) = Hq * blk / (P + blk).  Layer 1: block key j is e_j,
+    # its prefix keys are zero, and every query is c * e_t: a row gives key t the weight
+    # e^c / (e^c + P + blk - 1) and every other key 1 / (e^c + P + blk - 1).  So
+    #   delta(t) = Hq*blk*e^c/(e^c+n-1) - Hq*blk/n > 0,  delta(j != t) = Hq*blk/(e^c+n-1) - Hq*blk/n < 0
+    # with n = P + blk.  A flipped difference, a dropped prefix or the layers' caches swapped
+    # (layer 0's random prefix keys in layer 1) all change these values.
+    rng = np.random.default_rng(26)
+    B, blk, Hq, Hkv, d, S = 1, 8, 2, 1, 8, 16
+    P, t, c = 21, 5, 3.0
+    plen = np.array([P], dtype=np.int32)
+    kc0, table, _ = _paged_prefix(rng, B, Hkv, d, S, plen)                 # random, unused by Q0 = 0
+    kc1, table1, _ = _paged_prefix(rng, B, Hkv, d, S, plen, scale=0.0)     # zero prefix keys
+    assert np.array_equal(table, table1)
+    kb = np.zeros((B, blk, Hkv, d)); kb[0, :, 0, :] = np.eye(d)
+    q0 = np.zeros((B, blk, Hq, d))
+    q1 = np.zeros((B, blk, Hq, d)); q1[0, :, :, t] = c
+    delta = O.score_l01_full(q0, kb, q1, kb, kc0, kc1, table, plen, 1.0)
+    n = P + blk
+    i0 = Hq * blk / n
+    want = np.full(blk, Hq * blk / (math.exp(c) + n - 1) - i0)
+    want[t] = Hq * blk * math.exp(c) / (math.exp(c) + n - 1) - i0
+    np.testing.assert_allclose(delta[0], want, rtol=0, atol=1e-12)
+    assert delta[0, t] > 0 and np.all(np.delete(delta[0], t) < 0)
+
+
 # ------------------------------------------------------------------ selection
+def test_kth_boundary_hand_cases():
+    # masked scores, largest first: 0.9, 0.9, 0.5, 0.3, -0.1; the decoded 2.0 never counts.
+    # An ascending order, an off-by-one index or counting decoded positions changes one of these.
+    delta = np.array([0.3, 0.9, 2.0, 0.9, -0.1, 0.5])
+    masked = np.array([1, 1, 0, 1, 1, 1], dtype=np.uint8)
+    got = [O.kth_boundary(delta, masked, k) for k in range(1, 8)]
+    assert got == [0.9, 0.9, 0.5, 0.3, -0.1, -0.1, -0.1]     # k = 5 = m; k > m clips to m
+    assert math.isnan(O.kth_boundary(delta, masked, 0))
+    assert math.isnan(O.kth_boundary(delta, masked, -2))
+    assert math.isnan(O.kth_boundary(delta, np.zeros(6, np.uint8), 3))
+    # a score that is not a number ranks as minus infinity
+    dn = np.array([np.nan, 0.2, -np.inf, 0.1])
+    assert O.kth_boundary(dn, np.ones(4, np.uint8), 2) == 0.1
+    assert O.kth_boundary(dn, np.ones(4, np.uint8), 3) == -math.inf
+
+
+def test_kth_boundary_is_the_smallest_kept_score():
+    # against the selection (itself pinned by the lexsort brute force below): for every request
+    # with 0 < k, the boundary equals the smallest kept score and no unkept candidate is above it
+    rng = np.random.default_rng(12)
+    B, blk = 60, 16
+    delta = np.round(rng.standard_normal((B, blk)), 1)
+    masked = (rng.random((B, blk)) < 0.7).astype(np.uint8)
+    budget = rng.integers(0, blk + 3, size=B)
+    keep, kept = O.select_budget(delta, masked, budget)
+    for r in range(B):
+        t = O.kth_boundary(delta[r], masked[r], int(kept[r]))
+        if kept[r] == 0:
+            assert math.isnan(t)
+            continue
+        assert t == delta[r][keep[r] == 1].min()
+        rest = delta[r][(masked[r] == 1) & (keep[r] == 0)]
+        assert rest.size == 0 or rest.max() <= t
+
+
+def test_select_nan_ranks_below_every_number():
+    # NaN ranks as -inf: below every number, tied with -inf (lower position first), so exactly
+    # k tokens are kept and the mean/std of the adaptive rule turn NaN (no count above it)
+    delta = np.array([[np.nan, 0.5, -np.inf, np.nan, -3.0, np.inf]])
+    masked = np.ones((1, 6), dtype=np.uint8)
+    for k, want in [(1, [0, 0, 0, 0, 0, 1]), (2, [0, 1, 0, 0, 0, 1]), (3, [0, 1, 0, 0, 1, 1]),
+                    (4, [1, 1, 0, 0, 1, 1]), (5, [1, 1, 1, 0, 1, 1]), (6, [1] * 6)]:
+        keep, kept = O.select_budget(delta, masked, np.array([k]))
+        assert keep[0].tolist() == want and kept[0] == k, k
+    assert O.request_budget(delta[0], masked[0], None, ("adaptive", 0.5, 2, 16)) == 2
+    keep, kept = O.select_budget(delta, masked, None, ("adaptive", 0.5, 2, 16))
+    assert keep[0].tolist() == [0, 1, 0, 0, 0, 1] and kept[0] == 2
+
+
 def test_select_hand_example():
     delta = np.array([[0.1, 0.9, 0.5, 0.9, -0.2, 0.7, 0.0, 0.3]])
     masked = np.array([[1, 1, 1, 1, 1, 0, 1, 1]], dtype=np.uint8)
