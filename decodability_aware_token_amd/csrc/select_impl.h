@@ -6,8 +6,10 @@
 // Lane j holds block position j (blk <= 64) and its delta.  The budget is either the caller's
 // per-request integer or clamp(#{delta > mean + beta*std}, lo, hi) over the masked candidates,
 // with mean and population std reduced in f32 by a fixed xor butterfly.  The top-k is a
-// rank-by-count: rank_j = #{masked i : delta_i > delta_j, or delta_i == delta_j and i < j}, kept
-// iff rank_j < k_r.  This makes ties go to the lower position and needs no sorting network.
+// rank-by-count: rank_j = #{masked i : key_i > key_j, or key_i == key_j and i < j}, kept iff
+// rank_j < k_r, where key = delta, or -inf for a delta that is not a number.  This makes ties go
+// to the lower position and needs no sorting network; the keys are totally ordered, so the ranks
+// of the m_r candidates are 0..m_r-1 and exactly k_r of them are kept.
 #pragma once
 
 #include "device_common.h"
@@ -54,11 +56,12 @@ __device__ __forceinline__ Selection select_compute(const SelectArgs& a, int r, 
   }
   const int k = min(max(b, 0), m);
 
+  const float key = __builtin_isnan(dj) ? -INFINITY : dj;
   int rank = 0;
   for (int i = 0; i < blk; ++i) {
-    const float di = __shfl(dj, i, 64);
+    const float ki = __shfl(key, i, 64);
     const bool mi = (mbits >> i) & 1ull;
-    rank += (mi && (di > dj || (di == dj && i < lane))) ? 1 : 0;
+    rank += (mi && (ki > key || (ki == key && i < lane))) ? 1 : 0;
   }
   return Selection{mj && rank < k, k};
 }

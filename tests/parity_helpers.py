@@ -54,6 +54,7 @@ def fetch(fs: FocusStep) -> dict:
         "kept_pos": fs.kept_pos[:T].cpu().numpy(),
         "out": fs.out[:T].float().cpu().numpy().astype(np.float64),
         "out_bits": bf16_to_np(fs.out[:T]),
+        "q_rows": bf16_to_np(fs.q_rows[:T]),
         "lse": None if fs.lse is None else fs.lse[:T].cpu().numpy().astype(np.float64),
     }
     if fs.hidden_rows is not None:
@@ -83,6 +84,58 @@ def check_keep(gpu_keep, ref_keep, ref_delta, masked, rule, gpu_kept=None, ref_k
         assert np.array_equal(gpu_kept, gpu_keep.sum(axis=1))
     assert not np.any(gpu_keep & (1 - masked)), "a decoded token was kept"
     return excused
+
+
+def check_ragged(gpu, ref, B, excused, rule, gathered=None):
+    """Offsets, kept positions and (optionally) gathered rows of the GPU against the oracle's,
+    request by request.
+
+    gpu: dict with offsets, kept_pos (rows below min(T, cap)), keep; ref: dict with offsets,
+    kept_pos, keep (the oracle's).  excused: requests whose kept sets may differ (near-ties).
+      * the GPU's offsets are the running total of its own kept counts;
+      * offsets are bit-exact up to the first excused request (all of them for budgets that do
+        not depend on the scores: the counts then never differ);
+      * every request that is not excused has exactly the oracle's kept positions; an excused
+        one lists its own kept positions in ascending order;
+      * gathered = [(gpu_rows, oracle_rows, source), ...]: rows of requests that are not
+        excused equal the oracle's gathered rows; rows of excused requests equal
+        source[r, position].
+    """
+    goff, roff = gpu["offsets"].astype(np.int64), ref["offsets"].astype(np.int64)
+    gkept = gpu["keep"].astype(np.int64).sum(axis=1)
+    assert np.array_equal(goff, np.concatenate([[0], np.cumsum(gkept)])), "offsets != running total"
+    first = min(excused) if excused else B
+    assert np.array_equal(goff[: first + 1], roff[: first + 1]), "offsets differ before a near-tie"
+    if rule[0] == "fixed":
+        assert np.array_equal(goff, roff), "offsets differ"
+    lim_g, lim_r = len(gpu["kept_pos"]), len(ref["kept_pos"])
+    ex = set(int(r) for r in excused)
+    for r in range(B):
+        # rows at or past the GPU's capacity are not written: compare what it holds
+        gs = gpu["kept_pos"][min(goff[r], lim_g): min(goff[r + 1], lim_g)]
+        n = len(gs)
+        if r in ex:
+            want = np.nonzero(gpu["keep"][r])[0][:n]
+        else:
+            assert goff[r + 1] - goff[r] == roff[r + 1] - roff[r], f"request {r}: kept count"
+            want = ref["kept_pos"][min(roff[r], lim_r): min(roff[r + 1], lim_r)][:n]
+        assert np.array_equal(gs, want), f"request {r}: kept positions {gs} != {want}"
+        for si, (grows, rrows, src) in enumerate(gathered or ()):
+            gr = grows[min(goff[r], lim_g): min(goff[r + 1], lim_g)]
+            if r in ex:
+                wr = src[r, gs]
+            else:
+                wr = rrows[min(roff[r], lim_r): min(roff[r + 1], lim_r)][:n]
+            assert np.array_equal(gr, wr), f"request {r}: gathered rows of set {si} differ"
+
+
+def gathered_sets(gpu, st, ref_keep):
+    """(gpu rows, oracle rows, source) of the attention queries and, if gathered, the hidden
+    states: the oracle's compaction of the same sources under its own kept sets."""
+    sets = [(gpu["q_rows"], O.compact(ref_keep, st.q_att)[2], st.q_att)]
+    if "hidden_rows" in gpu:
+        sets.append((gpu["hidden_rows"], O.compact(ref_keep, st.hidden)[2], st.hidden))
+    return sets
 
 
 def rows_by_token(offsets, kept_pos, B, lim):
