@@ -14,7 +14,8 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfocus.so")
+# FOCUS_LIBRARY may name another build of the same library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("FOCUS_LIBRARY") or os.path.join(_PKG, "libfocus.so")
 
 FOCUS_OK = 0
 FOCUS_ERR_INVALID_ARG = -1

@@ -658,13 +658,21 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
                              __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      // the partial must be complete at device scope before the arrival is counted
+      // the partial must be complete at device scope before the arrival is counted: the
+      // compiler may not move the increment above the wait, and the wait returns only once
+      // every store of this wave has been acknowledged by the device-coherent level
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       int old = 0;
       if (lane == 0)
         old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = uni(old) == npieces - 1;
     }
+    // The merge's loads may not be hoisted above the counter value that selects this wave:
+    // issued after it has returned, device-scope loads see every partial whose arrival it
+    // counts (each was complete at that level before its increment).
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (!last) return;
     // last arrival: merge every piece in key order (own piece from registers), then reset the
     // counter for the next call.  The same operations whether a piece comes from registers or
