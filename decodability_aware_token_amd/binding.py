@@ -60,6 +60,11 @@ SIGNATURES = {
                                    [_c_float] + [_c_void_p] * 5 + [_c_int] +
                                    [_c_void_p] * 3 + [_c_int] + [_c_void_p] * 2 + [_c_int] +
                                    [_c_void_p, _c_size_t, _c_void_p]),
+    "focus_noalloc_scratch_bytes": (_c_size_t, []),
+    "focus_score_select_compact_noalloc": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 +
+                                           [_c_float] + [_c_void_p] * 5 + [_c_int] +
+                                           [_c_void_p] * 3 + [_c_int] + [_c_void_p] * 2 +
+                                           [_c_int, _c_void_p]),
     "focus_kv_writeback": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p] * 3),
     "focus_block_commit": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 2 +
                            [_c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -297,10 +302,12 @@ def _row_set_arrays(row_sets, gathered):
 
 def score_select_compact(q0, k0, q1, k1, sm_scale: float, masked, budget, row_sets, cap: int,
                          max_kept=None, delta=None, keep=None, kept_count=None, offsets=None,
-                         kept_pos=None, gathered=None, workspace=None):
+                         kept_pos=None, gathered=None, workspace=None, noalloc=False):
     """delta, keep, kept_count, offsets, kept_pos and the gathered row sets of
     focus_score_select with per-request budgets followed by focus_compact_multi, in two launches
-    (see focus_score_select_compact)."""
+    (see focus_score_select_compact).  noalloc=True calls focus_score_select_compact_noalloc,
+    which keeps its partials in the library's own device array (no workspace); the output
+    tensors are then best passed in, so that nothing is allocated here either."""
     B, blk, Hq, d = q0.shape
     Hkv = k0.shape[2]
     dev = q0.device
@@ -319,6 +326,14 @@ def score_select_compact(q0, k0, q1, k1, sm_scale: float, masked, budget, row_se
         gathered = [torch.empty((max(cap, 1),) + tuple(r.shape[2:]), dtype=r.dtype, device=dev)
                     for r in row_sets]
     rows_arr, bytes_arr, out_arr = _row_set_arrays(row_sets, gathered)
+    if noalloc:
+        rc = lib().focus_score_select_compact_noalloc(
+            _ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), dt, B, blk, Hq, Hkv, d, float(sm_scale),
+            _ptr(masked), _ptr(budget), _ptr(delta), _ptr(keep), _ptr(kept_count),
+            len(row_sets), rows_arr, bytes_arr, out_arr, int(cap), _ptr(offsets),
+            _ptr(kept_pos), int(blk if max_kept is None else max_kept), _stream(dev))
+        _check("focus_score_select_compact_noalloc", rc)
+        return delta, keep, kept_count, offsets, kept_pos, gathered
     need = lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d)
     workspace, wsb = _workspace(need, dev, workspace)
     rc = lib().focus_score_select_compact(

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "launch.h"
 
@@ -26,6 +27,34 @@ bool group_ok(int Hq, int Hkv) {
 }
 int status_of(hipError_t e) { return e == hipSuccess ? FOCUS_OK : FOCUS_ERR_HIP; }
 
+}  // namespace
+
+// Scratch of focus_score_select_compact_noalloc: the score partials [B, Hkv, blk] f32 live in
+// this array, one copy per GPU, held until the process ends.  Host code never uses the name
+// itself (on the host it is a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, looked up once per device.
+static constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or FOCUS_ERR_HIP.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FOCUS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return FOCUS_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FOCUS_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -225,17 +254,23 @@ int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const vo
                         stream);
 }
 
-int focus_score_select_compact(const void* q0, const void* k0, const void* q1, const void* k1,
-                               int dtype, int B, int blk, int Hq, int Hkv, int d, float sm_scale,
-                               const uint8_t* masked, const int32_t* budget, float* delta,
-                               uint8_t* keep, int32_t* kept_count, int nsets,
-                               const void* const* rows, const int64_t* row_bytes,
-                               void* const* gathered, int cap, int32_t* offsets,
-                               int32_t* kept_pos, int max_kept, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+namespace {
+// The two launches of focus_score_select_compact, validated and ready to go.
+struct FrontEnd {
+  focus::ScoreArgs sa;
+  focus::SelectCompactArgs a;
+};
+
+int front_end_prepare(const void* q0, const void* k0, const void* q1, const void* k1, int dtype,
+                      int B, int blk, int Hq, int Hkv, int d, float sm_scale,
+                      const uint8_t* masked, const int32_t* budget, float* delta, uint8_t* keep,
+                      int32_t* kept_count, int nsets, const void* const* rows,
+                      const int64_t* row_bytes, void* const* gathered, int cap,
+                      int32_t* offsets, int32_t* kept_pos, int max_kept, void* workspace,
+                      size_t workspace_bytes, FrontEnd& fe) {
   if (!masked || !budget || !keep || !kept_count) return FOCUS_ERR_INVALID_ARG;
   if (max_kept < 1 || max_kept > blk) return FOCUS_ERR_INVALID_ARG;
-  focus::ScoreArgs sa;
+  focus::ScoreArgs& sa = fe.sa;
   int rc = score_prepare(q0, k0, q1, k1, nullptr, nullptr, dtype, B, blk, Hq, Hkv, d, sm_scale,
                          delta, workspace, workspace_bytes, sa);
   if (rc != FOCUS_OK) return rc;
@@ -244,9 +279,8 @@ int focus_score_select_compact(const void* q0, const void* k0, const void* q1, c
   if (rc != FOCUS_OK) return rc;
   if (!aligned4(masked)) return FOCUS_ERR_INVALID_ARG;
   sa.partial_only = 1;
-  hipError_t e = focus::launch_score(sa, stream);
-  if (e != hipSuccess) return FOCUS_ERR_HIP;
-  focus::SelectCompactArgs a{};
+  focus::SelectCompactArgs& a = fe.a;
+  a = focus::SelectCompactArgs{};
   a.part = sa.part;
   a.Hkv = Hkv;
   a.delta = delta;
@@ -264,7 +298,59 @@ int focus_score_select_compact(const void* q0, const void* k0, const void* q1, c
   const int64_t per_wg = 256 * 8 * 16;
   a.nsplit = (int)std::min<int64_t>(
       16, std::max<int64_t>(1, (max_kept * bytes + per_wg - 1) / per_wg));
-  return status_of(focus::launch_select_compact(a, stream));
+  return FOCUS_OK;
+}
+
+int front_end_launch(const FrontEnd& fe, hipStream_t stream) {
+  if (focus::launch_score(fe.sa, stream) != hipSuccess) return FOCUS_ERR_HIP;
+  return status_of(focus::launch_select_compact(fe.a, stream));
+}
+
+}  // namespace
+
+int focus_score_select_compact(const void* q0, const void* k0, const void* q1, const void* k1,
+                               int dtype, int B, int blk, int Hq, int Hkv, int d, float sm_scale,
+                               const uint8_t* masked, const int32_t* budget, float* delta,
+                               uint8_t* keep, int32_t* kept_count, int nsets,
+                               const void* const* rows, const int64_t* row_bytes,
+                               void* const* gathered, int cap, int32_t* offsets,
+                               int32_t* kept_pos, int max_kept, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  FrontEnd fe;
+  const int rc = front_end_prepare(q0, k0, q1, k1, dtype, B, blk, Hq, Hkv, d, sm_scale, masked,
+                                   budget, delta, keep, kept_count, nsets, rows, row_bytes,
+                                   gathered, cap, offsets, kept_pos, max_kept, workspace,
+                                   workspace_bytes, fe);
+  if (rc != FOCUS_OK) return rc;
+  return front_end_launch(fe, stream);
+}
+
+size_t focus_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int focus_score_select_compact_noalloc(const void* q0, const void* k0, const void* q1,
+                                       const void* k1, int dtype, int B, int blk, int Hq,
+                                       int Hkv, int d, float sm_scale, const uint8_t* masked,
+                                       const int32_t* budget, float* delta, uint8_t* keep,
+                                       int32_t* kept_count, int nsets, const void* const* rows,
+                                       const int64_t* row_bytes, void* const* gathered, int cap,
+                                       int32_t* offsets, int32_t* kept_pos, int max_kept,
+                                       hipStream_t stream) {
+  // every argument is checked before the device is touched; the partials must fit the array
+  if (B > 0 && blk > 0 && Hkv > 0 && focus::score_workspace_bytes(B, blk, Hkv) > kScratchBytes)
+    return FOCUS_ERR_UNSUPPORTED;
+  FrontEnd fe;
+  // validated against a stand-in workspace of the scratch's size (never dereferenced)
+  int rc = front_end_prepare(q0, k0, q1, k1, dtype, B, blk, Hq, Hkv, d, sm_scale, masked,
+                             budget, delta, keep, kept_count, nsets, rows, row_bytes, gathered,
+                             cap, offsets, kept_pos, max_kept, reinterpret_cast<void*>(256),
+                             kScratchBytes, fe);
+  if (rc != FOCUS_OK) return rc;
+  void* ptr = nullptr;
+  rc = scratch_address(&ptr);
+  if (rc != FOCUS_OK) return rc;
+  fe.sa.part = static_cast<float*>(ptr);
+  fe.a.part = static_cast<const float*>(ptr);
+  return front_end_launch(fe, stream);
 }
 
 size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, int d, int S,

@@ -9,7 +9,8 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory owned by the caller, unless stated otherwise.
- *     The library never allocates, frees or retains memory.
+ *     No call allocates, frees or retains memory; the one memory the library owns is the fixed
+ *     device array of call 3c, which exists from the moment its code is loaded on a GPU.
  *   - Every call is asynchronous on `stream` (0 = the default stream). No call synchronises
  *     the host; ragged sizes (kept counts, offsets, prefix lengths) never leave the device.
  *   - A negative return value is a host-detected argument error: nothing was launched.
@@ -104,7 +105,8 @@ int focus_score_l01_lse(const void* q0, const void* k0, const void* q1, const vo
  *   adaptive != 0:  over the candidates, mu = mean(delta), sigma = population std (both f32),
  *                   c = #{delta > mu + beta*sigma}, b_r = min(max(c, lo), hi)
  *   k_r = min(max(b_r, 0), m_r); the k_r candidates with the largest delta are kept, equal
- *   deltas ordered by lower position first.  Decoded positions are never kept.
+ *   deltas ordered by lower position first, a delta that is not a number ranked as -infinity
+ *   (so exactly k_r are kept).  Decoded positions are never kept.
  *
  *   delta       [B, blk] f32         masked [B, blk] u8      budget [B] i32 (ignored if adaptive)
  *   keep        [B, blk] u8 output (1 = kept)                kept_count [B] i32 output
@@ -183,6 +185,33 @@ int focus_score_select_compact(const void* q0, const void* k0, const void* q1, c
                                void* const* gathered, int cap, int32_t* offsets,
                                int32_t* kept_pos, int max_kept, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
+ * 3c. focus_score_select_compact for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The same launches and results as focus_score_select_compact, without the workspace
+ * arguments: the per-kv-head score partials (B*Hkv*blk*4 bytes) live in a library-owned device
+ * array of focus_noalloc_scratch_bytes() bytes (4 MiB), one per GPU, which exists once the
+ * library's code is loaded on that GPU and is held until the process ends.  The call allocates
+ * nothing; its first call on a GPU looks the array's address up (issue that one before any
+ * graph capture).  The partials need no initialisation, so nothing is cleared between calls.
+ * All calls on one GPU share the array and it keeps the last call's contents: calls that may
+ * overlap in time on the same GPU (several streams or threads) race on it and must not be
+ * issued.
+ * Returns FOCUS_ERR_UNSUPPORTED when B*Hkv*blk*4 exceeds the array (B = 4096, Hkv = 8, blk = 32
+ * fits exactly), FOCUS_ERR_HIP if the array's address cannot be found; everything else as
+ * focus_score_select_compact.
+ * ------------------------------------------------------------------------------------------ */
+size_t focus_noalloc_scratch_bytes(void);
+int focus_score_select_compact_noalloc(const void* q0, const void* k0, const void* q1,
+                                       const void* k1, int dtype, int B, int blk, int Hq,
+                                       int Hkv, int d, float sm_scale, const uint8_t* masked,
+                                       const int32_t* budget, float* delta, uint8_t* keep,
+                                       int32_t* kept_count, int nsets, const void* const* rows,
+                                       const int64_t* row_bytes, void* const* gathered, int cap,
+                                       int32_t* offsets, int32_t* kept_pos, int max_kept,
+                                       hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------------
  * 4. Ragged paged attention of the kept queries.

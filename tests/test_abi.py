@@ -162,6 +162,36 @@ def test_score_select_compact_errors():
     assert _ssc(mk=33) == F.FOCUS_ERR_INVALID_ARG             # max_kept > blk
 
 
+def _ssc_noalloc(**kw):
+    import ctypes
+    a = dict(q0=P, k0=P, q1=P, k1=P, dt=1, B=4, blk=32, Hq=32, Hkv=8, d=128, sc=0.1, msk=P,
+             bud=P, delta=P, keep=P, kc=P, n=1, rows=[P], rb=[8192], gat=[P], cap=128, off=P,
+             pos=P, mk=4)
+    a.update(kw)
+    n = max(len(a["rows"]), 1)
+    rows = (ctypes.c_void_p * n)(*a["rows"])
+    rb = (ctypes.c_int64 * n)(*a["rb"])
+    gat = (ctypes.c_void_p * n)(*a["gat"])
+    return F.lib().focus_score_select_compact_noalloc(
+        a["q0"], a["k0"], a["q1"], a["k1"], a["dt"], a["B"], a["blk"], a["Hq"], a["Hkv"], a["d"],
+        a["sc"], a["msk"], a["bud"], a["delta"], a["keep"], a["kc"], a["n"], rows, rb, gat,
+        a["cap"], a["off"], a["pos"], a["mk"], None)
+
+
+def test_score_select_compact_noalloc_errors():
+    # every check happens before the device is touched (these calls return without a GPU)
+    assert F.lib().focus_noalloc_scratch_bytes() == 4 << 20
+    # the partials B*Hkv*blk*4 bytes must fit the 4 MiB array: 4096*8*32*4 fits exactly
+    assert _ssc_noalloc(B=4096, Hkv=16, Hq=32, q0=None) == F.FOCUS_ERR_UNSUPPORTED
+    assert _ssc_noalloc(B=4096, blk=64, Hq=32, Hkv=8) == F.FOCUS_ERR_UNSUPPORTED
+    assert _ssc_noalloc(B=4096, q0=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc_noalloc(bud=None) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc_noalloc(msk=P + 2) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc_noalloc(blk=20) == F.FOCUS_ERR_UNSUPPORTED
+    assert _ssc_noalloc(mk=33) == F.FOCUS_ERR_INVALID_ARG
+    assert _ssc_noalloc(B=0) == F.FOCUS_ERR_INVALID_ARG
+
+
 def _attn(**kw):
     a = dict(q=P, off=P, cap=64, kc=P, vc=P, npages=100, pt=P, maxp=16, pl=P, kb=P, vb=P, B=4,
              blk=32, Hq=32, Hkv=8, d=128, S=64, mk=4, sc=0.088, out=P, lse=P, ws=P,
