@@ -56,27 +56,52 @@ def test_profile_summary_scales_counters_by_the_copy(tmp_path, monkeypatch):
     out = tmp_path / "out"
     attn = "void focus::(anonymous namespace)::attn_kernel<128, 1, 2, true>(focus::Params)"
     copy = "__amd_rocclr_copyBuffer(void*)"
+    w = out / "sdar_b256_blk32"
     # the copy of 1 GiB reads as half its bytes in FETCH_SIZE and all of them in WRITE_SIZE
-    _write_pmc(out / "pmc" / "copy_fetch", "FETCH_SIZE", [(copy, 524288.0), (copy, 12.0)])
-    _write_pmc(out / "pmc" / "copy_write", "WRITE_SIZE", [(copy, 1048576.0)])
-    _write_pmc(out / "pmc" / "step_fetch", "FETCH_SIZE",
-               [(attn, 1000.0), (attn, 3000.0), (attn, 2000.0)])      # median 2000 KiB
-    _write_pmc(out / "pmc" / "step_write", "WRITE_SIZE", [(attn, 10.0)])
-    os.makedirs(out / "prof")
-    with open(out / "prof" / "trace_kernel_stats.csv", "w", newline="") as fh:
-        w = csv.writer(fh)
-        w.writerow(["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
-        w.writerow([attn, 3, 150000, 140000, 160000, 80.0])
+    _write_pmc(out / "calib" / "fetch", "FETCH_SIZE", [(copy, 524288.0), (copy, 12.0)])
+    _write_pmc(out / "calib" / "write", "WRITE_SIZE", [(copy, 1048576.0)])
+    _write_pmc(w / "fetch", "FETCH_SIZE", [(attn, 1000.0), (attn, 3000.0), (attn, 2000.0)])
+    _write_pmc(w / "write", "WRITE_SIZE", [(attn, 10.0)])
+    # MFMA: busy cycles over (active cycles of one XCD x 1024 SIMDs); bf16 work in 512-flop units
+    os.makedirs(w / "mfma")
+    with open(w / "mfma" / "run_counter_collection.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writerow([0, attn, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000 * 0.25])
+        wr.writerow([0, attn, "GRBM_GUI_ACTIVE", 8 * 1000])     # summed over the 8 XCDs
+        wr.writerow([0, attn, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2.0e6])
+    os.makedirs(w / "trace")
+    with open(w / "trace" / "run_kernel_stats.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        wr.writerow([attn, 3, 150000, 140000, 160000, 80.0])
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
-    bench.summarize_profiles(str(out), "w")
-    rec = json.load(open(tmp_path / "profiles" / "attn_traffic_w.json"))
+    bench.summarize_profiles(str(out), "sdar_b256_blk32")
+    rec = json.load(open(tmp_path / "profiles" / "attn_traffic_sdar_b256_blk32.json"))
     assert rec["kernel"] == "attn_kernel<128, 1, 2, true>"
     assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
     assert rec["hbm_read_bytes"] == 2000 * 1024 * 2
     assert rec["hbm_write_bytes"] == 10 * 1024
-    table = open(tmp_path / "profiles" / "kernels_w.txt").read()
+    assert abs(rec["mfma_busy_frac"] - 0.25) < 1e-9
+    assert rec["mfma_bf16_flops_per_launch"] == 2.0e6 * 512
+    assert rec["trace_avg_us"] == 150.0
+    table = open(tmp_path / "profiles" / "kernels_sdar_b256_blk32.txt").read()
     assert "attn_kernel<128, 1, 2, true>" in table and "150.00" in table
+
+
+def test_focused_attention_instantiation_per_recipe():
+    from workloads import BY_NAME
+    assert bench.focused_attn_kernel(BY_NAME["sdar_b256_blk32"]) == "attn_kernel<128, 1, 2, true>"
+    assert bench.focused_attn_kernel(BY_NAME["sdar_b32_blk32"]) == "attn_kernel<128, 2, 2, true>"
+    assert bench.focused_attn_kernel(BY_NAME["sweep_b128_blk64"]) == "attn_kernel<128, 4, 2, true>"
+    assert bench.focused_attn_kernel(BY_NAME["tiny_b2_blk16"]) == "attn_kernel<64, 1, 2, true>"
+
+
+def test_host_cpu_description():
+    cpu = bench.host_cpu()
+    assert cpu["logical_cpus"] >= 1 and 1 <= cpu["physical_cores"] <= cpu["logical_cpus"]
+    assert 1 <= cpu["workers"] <= cpu["logical_cpus"] and cpu["model"]
 
 
 def test_counter_traffic_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
