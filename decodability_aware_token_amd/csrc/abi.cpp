@@ -382,6 +382,8 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
   if ((d != 64 && d != 128) || !pow2_in(S, 16, 64) || !pow2_in(blk, 16, 64) || B > kMaxB)
     return FOCUS_ERR_UNSUPPORTED;
   if ((long long)max_pages * S > (1LL << 24)) return FOCUS_ERR_UNSUPPORTED;
+  // (page, kv head) block indices are 32-bit in the kernel
+  if ((long long)num_pages * Hkv >= (1LL << 32)) return FOCUS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)))
     return FOCUS_ERR_INVALID_ARG;

@@ -48,6 +48,9 @@ constexpr int kWaves = 4;  // waves per workgroup
 // accesses more local, and the CU's outstanding misses are the limit, not the wave count.
 constexpr int kPrefetchQt1 = 2;
 constexpr int kWgsPerCuQt1 = 1;
+// Shared tiles: tiles whose shares are in flight per workgroup, and workgroups per CU.
+constexpr int kShPrefetch = 2;
+constexpr int kShWgsPerCu = 2;
 // cache-policy bits of a vector memory access with device scope (SC1): stores write through to
 // the device-coherent level, loads read from it (what device-scope atomics use on gfx950)
 constexpr int kCpolDevice = 16;
@@ -85,6 +88,14 @@ struct Params {
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int X>
+constexpr int kLog2() {
+  static_assert(X > 0 && (X & (X - 1)) == 0, "power of two");
+  int l = 0;
+  while ((1 << l) < X) ++l;
+  return l;
+}
 
 template <int D>
 struct Tile {
@@ -139,12 +150,15 @@ __device__ __forceinline__ void advance(Cursor& c, const Meta& m, const Params& 
 struct Pages {
   int a, b;
 };
+// Branch-free (indices clamped into the request's row; a block tile reads its row's first entry
+// and ignores it), so that the loads can be issued at the start of a step, ahead of the work
+// that does not need them.  A table without columns (max_pages == 0) is never read.
 __device__ __forceinline__ Pages fetch_pages(const Cursor& c, const Params& p,
                                              const int32_t* __restrict__ page_table) {
   Pages pg{0, 0};
-  if (c.tt < c.ntp()) {
-    const int p0 = (c.tt * 32) >> p.log2S;
-    const int last = (c.plen() - 1) >> p.log2S;
+  if (p.max_pages > 0) {
+    const int last = max((c.plen() - 1) >> p.log2S, 0);
+    const int p0 = min((c.tt * 32) >> p.log2S, last);
     const int32_t* row = page_table + (size_t)c.r * p.max_pages;
     pg.a = row[p0];
     pg.b = row[min(p0 + 1, last)];
@@ -176,7 +190,7 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
   // per tile with wave-uniform (scalar) arithmetic; a lane then picks one of two bases.  A tile
   // of 32 keys starts at a multiple of 32, so with S >= 32 (and in the block) it lies in one
   // block: only S = 16 uses the second.
-  const size_t blk_elems = (size_t)D << log2S;  // one (page, kv head) block
+  const int blk_shift = kLog2<D>() + log2S;  // log2 of one (page, kv head) block's elements
   const uint16_t *k0p, *k1p, *v0p, *v1p;
   bool bad = false;
   if (paged) {
@@ -185,14 +199,16 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
     bad = !oka || !okb;
     a = oka ? a : 0;
     b = okb ? b : 0;
-    const size_t oa = ((size_t)a * p.Hkv + c.g) * blk_elems;
-    const size_t ob = ((size_t)b * p.Hkv + c.g) * blk_elems;
+    // (page, kv head) block index times the block size, a power of two: a 32-bit index and
+    // one 64-bit shift (page ids are below num_pages, so the index fits)
+    const size_t oa = (size_t)(uint32_t)(a * p.Hkv + c.g) << blk_shift;
+    const size_t ob = (size_t)(uint32_t)(b * p.Hkv + c.g) << blk_shift;
     k0p = p.k_cache + oa;
     k1p = p.k_cache + ob;
     v0p = p.v_cache + oa;
     v1p = p.v_cache + ob;
   } else {
-    const size_t o = ((size_t)c.r * p.Hkv + c.g) * blk_elems;
+    const size_t o = (size_t)(uint32_t)(c.r * p.Hkv + c.g) << blk_shift;
     k0p = k1p = p.k_blk + o;
     v0p = v1p = p.v_blk + o;
   }
@@ -222,6 +238,119 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
     const u32x2_t hi = load8_stream(vp[1] + 16 * dt * 8);
     T.v[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   }
+}
+
+// Shared tiles.  When an item's rows need several query groups, the four waves of a workgroup
+// are four query groups of the same kv head: they stream the same tiles, so the workgroup loads
+// each tile once.  Every thread loads a 1/256 share of a tile (D/64 chunks of 16 bytes of K and
+// as many of V) into registers NB tiles ahead of use; the shares pass through a ring of three
+// LDS tile buffers, one barrier per tile, and each wave reads its MFMA fragments from LDS.
+// Tile buffer layout (16-byte chunks): K chunk (dim group c, key k) at c*32 + k, then V chunk
+// (key group q, dim e) at 4*D + q*D + e -- the global layouts restricted to the tile's 32 keys.
+constexpr int kShBufs = 3;
+
+template <int D>
+struct Share {
+  static constexpr int NC = D / 64;  // 16-byte chunks of K, and of V, per thread
+  u32x4_t k[NC], v[NC];
+  bool bad;  // a page id of the tile was out of range (page 0 was read instead)
+};
+
+// This thread's share of the cursor's tile, branch-free and clamped like load_tile: K chunks
+// of keys past the valid length hold the last valid key, V chunks of key groups past it hold
+// the last valid group (compute_tile masks both).
+template <int D, bool WO>
+__device__ __forceinline__ void load_share(Share<D>& sh, const Cursor& c, Pages pg,
+                                           const Params& p, int tid) {
+  constexpr int NC = D / 64;
+  const int ntp = c.ntp();
+  const bool paged = c.tt < ntp;
+  const int key0 = paged ? c.tt * 32 : (c.tt - ntp) * 32;
+  const int nvalid = paged ? c.plen() : p.blk;
+  const int log2S = paged ? p.log2S : p.log2blk;
+  const int S = 1 << log2S;
+  const int last = nvalid - 1;
+  const int blk_shift = kLog2<D>() + log2S;  // log2 of one (page, kv head) block's elements
+  const uint16_t *k0p, *k1p, *v0p, *v1p;
+  bool bad = false;
+  if (paged) {
+    int a = pg.a, b = pg.b;
+    const bool oka = a >= 0 && a < p.num_pages, okb = b >= 0 && b < p.num_pages;
+    bad = !oka || !okb;
+    a = oka ? a : 0;
+    b = okb ? b : 0;
+    // (page, kv head) block index times the block size, a power of two: a 32-bit index and
+    // one 64-bit shift (page ids are below num_pages, so the index fits)
+    const size_t oa = (size_t)(uint32_t)(a * p.Hkv + c.g) << blk_shift;
+    const size_t ob = (size_t)(uint32_t)(b * p.Hkv + c.g) << blk_shift;
+    k0p = p.k_cache + oa;
+    k1p = p.k_cache + ob;
+    v0p = p.v_cache + oa;
+    v1p = p.v_cache + ob;
+  } else {
+    const size_t o = (size_t)(uint32_t)(c.r * p.Hkv + c.g) << blk_shift;
+    k0p = k1p = p.k_blk + o;
+    v0p = v1p = p.v_blk + o;
+  }
+  const int p0 = key0 >> log2S;
+  const bool two = paged && S < 32;
+  sh.bad = bad;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int i = tid + 256 * u;
+    const int key = min(key0 + (i & 31), last);
+    const uint16_t* kb = (two && (key >> log2S) != p0) ? k1p : k0p;
+    const uint16_t* ka = kb + ((uint32_t)(((i >> 5) << log2S) + (key & (S - 1))) << 3);
+    sh.k[u] = load16_stream(ka);
+  }
+  if constexpr (!WO) return;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int j = tid + 256 * u;
+    const int grp = min(key0 + 8 * (j / D), last & ~7);
+    const uint16_t* vb = (two && (grp >> log2S) != p0) ? v1p : v0p;
+    const uint16_t* va = vb + ((uint32_t)(((grp & (S - 1)) >> 3) * D + (j & (D - 1))) << 3);
+    sh.v[u] = load16_stream(va);
+  }
+}
+
+template <int D, bool WO>
+__device__ __forceinline__ void store_share(const Share<D>& sh, u32x4_t* buf, int tid) {
+  constexpr int NC = D / 64;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) buf[tid + 256 * u] = sh.k[u];
+  if constexpr (WO) {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) buf[4 * D + tid + 256 * u] = sh.v[u];
+  }
+}
+
+// The wave's MFMA fragments of a tile from its LDS buffer: the registers load_tile fills.
+template <int D, bool WO>
+__device__ __forceinline__ void read_tile(Tile<D>& T, const u32x4_t* buf, int lane) {
+  constexpr int NK = D / 32, ND = D / 16;
+  const int m16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) T.k[s][kk] = buf[(4 * kk + j4) * 32 + 16 * s + m16];
+  if constexpr (!WO) return;
+  const u32x2_t* v8 = reinterpret_cast<const u32x2_t*>(buf + 4 * D);
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    const u32x2_t lo = v8[((j4 >> 1) * D + 16 * dt + m16) * 2 + (j4 & 1)];
+    const u32x2_t hi = v8[((2 + (j4 >> 1)) * D + 16 * dt + m16) * 2 + (j4 & 1)];
+    T.v[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+// Workgroup barrier for the LDS tile ring: this wave's LDS writes are complete, and the
+// compiler moves no memory access across it (no wait on the vector memory loads in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // The B operand (Q^T) of the current item.  With up to two query tiles it lives in registers;
@@ -437,8 +566,10 @@ __device__ __forceinline__ int slice_begin(int i, int total, int n) {
 }
 
 // page_table is a separate restrict argument so that its (uniform) reads become scalar loads.
-template <int D, int QT, int NB, bool WO>
-__global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel(
+// SH: shared tiles (the workgroup's four waves are four query groups of one kv head; NB is then
+// the number of tiles whose shares are in flight in registers).
+template <int D, int QT, int NB, bool WO, bool SH>
+__global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void attn_kernel(
     Params p, const int32_t* __restrict__ page_table) {
   constexpr int NK = D / 32, ND = D / 16, R = 16 * QT;
   extern __shared__ __align__(16) int smem_i[];
@@ -831,6 +962,66 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
     ++idx;
   };
   bool bad = false;
+  if constexpr (SH) {
+    // ---- shared tiles: shares of tiles tv+1 .. tv+NB are in flight in registers while tile tv
+    // is computed from LDS buffer tv % 3.  At step tv the share of tile tv+1 is written to
+    // buffer (tv+1) % 3 -- last read by the computation of tile tv-2, which every wave had
+    // finished before the previous step's barrier -- and its registers take tile tv+1+NB;
+    // after the barrier every share of tile tv is in LDS.  All four waves take the same steps.
+    constexpr int CH = 8 * D;  // 16-byte chunks per tile buffer (K, then V)
+    u32x4_t* ring = reinterpret_cast<u32x4_t*>(s_q);
+    Share<D> sh[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (k > 0 && tvl + 1 < n) next(L, tvl);
+      load_share<D, WO>(sh[k], L, fetch_pages(L, p, page_table), p, tid);
+    }
+    if (tvl + 1 < n) next(L, tvl);
+    store_share<D, WO>(sh[0], ring, tid);
+    int badbits = sh[0].bad ? 1 : 0;  // bit i: the tile in buffer i read an invalid page id
+    load_share<D, WO>(sh[0], L, fetch_pages(L, p, page_table), p, tid);
+    if (tvl + 1 < n) next(L, tvl);
+    lds_barrier();
+    int tv = 0;
+    auto sh_step = [&](Share<D>& Y) {
+      const bool live = tv < n;
+      const Pages pg = fetch_pages(L, p, page_table);  // in flight during the LDS writes
+      if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
+      const int wb = (tv + 1) % kShBufs;
+      store_share<D, WO>(Y, ring + (size_t)wb * CH, tid);
+      badbits = (badbits & ~(1 << wb)) | ((Y.bad ? 1 : 0) << wb);
+      load_share<D, WO>(Y, L, pg, p, tid);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      lds_barrier();
+      if (live) {
+        const int rb = tv % kShBufs;
+        const int nq = (C.nrows - C.qg * R + 15) >> 4;
+        if (nq > 0) {
+          Tile<D> X;
+          read_tile<D, WO>(X, ring + (size_t)rb * CH, lane);
+          const int ntp = C.ntp();
+          const bool pg = C.tt < ntp;
+          compute_tile<D, QT, WO>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk,
+                                  nq, qf, o, mrun, lrun, p.scale_log2, lane);
+        }
+        bad = bad || ((badbits >> rb) & 1);
+        if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
+          finalize(C, bad);
+          reset();
+          bad = false;
+        }
+      }
+      if (tvc + 1 < n) next(C, tvc);
+      if (tvl + 1 < n) next(L, tvl);
+      ++tv;
+    };
+    while (true) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) sh_step(sh[(j + 1) % NB]);
+      if (tv >= n) break;
+    }
+    return;
+  }
   Tile<D> tl[NB];
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k) {
@@ -845,8 +1036,9 @@ __global__ __launch_bounds__(256, (NB == 2 && QT == 1) ? 2 : 1) void attn_kernel
   // merge the roles' pending loads at the loop head and drain the prefetch there.
   auto step = [&](Tile<D>& X, Tile<D>& Y) {
     const bool live = tv < n;
+    const Pages pg = fetch_pages(L, p, page_table);
     if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
-    load_tile<D, WO>(Y, L, fetch_pages(L, p, page_table), p, lane);
+    load_tile<D, WO>(Y, L, pg, p, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     if (live) {
       const int ntp = C.ntp();
@@ -892,12 +1084,13 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int D, int QT, bool WO>
+template <int D, int QT, bool WO, bool SH = false>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
   size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
   if (QT >= 4) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
-  constexpr int NB = QT == 1 ? kPrefetchQt1 : 2;
-  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO>), dim3(plan.wgs), dim3(256), shmem, s, prm,
+  if (SH) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kShBufs * 8 * D * 16;
+  constexpr int NB = SH ? kShPrefetch : (QT == 1 ? kPrefetchQt1 : 2);
+  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH>), dim3(plan.wgs), dim3(256), shmem, s, prm,
                      prm.page_table);
   return hipGetLastError();
 }
@@ -909,14 +1102,24 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
   AttnPlan pl{};
   const int G = Hq / Hkv;
   const int rows = max_kept * G;
-  pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-  pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
-  // one 4-wave workgroup per CU (one wave per SIMD, each with NB tiles of 32 keys in flight);
-  // without the output the larger query tiles are light enough for two per CU, which hides
-  // their instruction latencies behind each other
   const int cus = device_cus();
-  pl.wgs = cus * kWgsPerCuQt1;
-  if (pl.qt > 1) pl.wgs = cus * (lse_only ? 2 : 1);
+  if (rows <= 32 || rows > 64) {
+    // one wave per item: 16, 32 or 64 rows (several query groups per (request, kv head) past
+    // 64 rows).  Up to 32 rows, one 4-wave workgroup per CU (one wave per SIMD, each with NB
+    // tiles of 32 keys in flight); 64-row waves also one per CU with the output, while without
+    // it the larger query tiles are light enough for two workgroups per CU.
+    pl.shared = false;
+    pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
+    pl.wgs = cus * ((pl.qt > 1 && lse_only) ? 2 : kWgsPerCuQt1);
+  } else {
+    // 33..64 rows: shared tiles, 16 rows per wave, the four waves of a workgroup on one
+    // (request, kv head)'s tiles, two workgroups per CU
+    pl.shared = true;
+    pl.qt = 1;
+    pl.nqg = kWaves;
+    pl.wgs = cus * kShWgsPerCu;
+  }
   const long long ntiles_max = ((long long)max_pages * S + 31) / 32 + (blk + 31) / 32;
   pl.tiles_bound = (long long)B * ntiles_max;
   pl.gs = Hkv * pl.nqg;
@@ -979,6 +1182,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
   prm.ws_o_bytes = (int)plan.ws_o_bytes;
   prm.ws_ml = reinterpret_cast<float*>(ws + plan.cnt_bytes + plan.ws_o_bytes);
   if (a.out == nullptr) {  // log-sum-exp only
+    if (plan.shared)
+      return a.d == 64 ? launch_dq<64, 1, false, true>(prm, plan, s)
+                       : launch_dq<128, 1, false, true>(prm, plan, s);
     if (a.d == 64) {
       if (plan.qt == 1) return launch_dq<64, 1, false>(prm, plan, s);
       if (plan.qt == 2) return launch_dq<64, 2, false>(prm, plan, s);
@@ -988,6 +1194,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
     if (plan.qt == 2) return launch_dq<128, 2, false>(prm, plan, s);
     return launch_dq<128, 4, false>(prm, plan, s);
   }
+  if (plan.shared)
+    return a.d == 64 ? launch_dq<64, 1, true, true>(prm, plan, s)
+                     : launch_dq<128, 1, true, true>(prm, plan, s);
   if (a.d == 64) {
     if (plan.qt == 1) return launch_dq<64, 1, true>(prm, plan, s);
     if (plan.qt == 2) return launch_dq<64, 2, true>(prm, plan, s);

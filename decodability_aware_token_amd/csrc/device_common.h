@@ -58,6 +58,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate with vmcnt = 0 and the other counters at their maxima (GFX9 encoding):
 // waits until every vector memory access of the wave, stores included, has completed
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate with lgkmcnt = 0 and the other counters at their maxima: waits until the
+// wave's LDS (and scalar memory) accesses have completed, not for its vector memory accesses
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 
 // Global-memory views of device pointers: loads through them are global (never flat)
 // instructions, which the compiler's wait counting can order with the other vector loads
@@ -69,6 +72,7 @@ typedef const __attribute__((address_space(1))) u32x4_t global_u32x4_t;
 __device__ __forceinline__ u32x2_t load8_stream(const void* p) {
   return __builtin_nontemporal_load((global_u32x2_t*)p);
 }
+
 
 // 16-byte load of data read exactly once (non-temporal: the caches do not keep it)
 __device__ __forceinline__ u32x4_t load16_stream(const void* p) {

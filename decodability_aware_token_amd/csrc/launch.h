@@ -85,7 +85,8 @@ struct AttnArgs {
   void* workspace;
 };
 struct AttnPlan {
-  int qt;                // 16-row query tiles per work item (1, 2 or 4)
+  bool shared;           // the four waves of a workgroup share each tile (several query groups)
+  int qt;                // 16-row query tiles per wave (1, 2 or 4)
   int nqg;               // query groups per (request, kv head) at max_kept
   int wgs;               // persistent workgroups (4 waves each)
   int gs;                // waves per column group: one per (kv head, query group)

@@ -246,7 +246,8 @@ int focus_score_select_compact_noalloc(const void* q0, const void* k0, const voi
  *               concurrently; calls of different shapes may share one.  The size depends on the
  *               current device's compute-unit count.
  * Supported: d in {64,128}; S in {16,32,64}; blk in {16,32,64}; Hq/Hkv in {1,2,4,8};
- *            1 <= max_kept <= blk; 1 <= B <= 4096; max_pages*S <= 2^24; fewer than 2^31 key
+ *            1 <= max_kept <= blk; 1 <= B <= 4096; max_pages*S <= 2^24; num_pages*Hkv < 2^32;
+ *            fewer than 2^31 key
  *            tiles of 32 over all (request, kv head, query group) at the longest prefixes;
  *            pointers 16-byte aligned.
  * ------------------------------------------------------------------------------------------ */

@@ -219,6 +219,7 @@ def test_attn_errors():
     assert _attn(Hq=64, Hkv=4) == F.FOCUS_ERR_UNSUPPORTED     # G = 16
     assert _attn(out=P + 4) == F.FOCUS_ERR_INVALID_ARG
     assert _attn(maxp=1 << 20) == F.FOCUS_ERR_UNSUPPORTED
+    assert _attn(npages=(1 << 31) - 1, Hkv=8, Hq=32) == F.FOCUS_ERR_UNSUPPORTED  # 32-bit blocks
     # long prefixes need a split workspace
     need = F.attn_workspace_bytes(4, 32, 32, 8, 128, 64, 128, 4)
     assert need > 0
@@ -240,6 +241,23 @@ def test_attn_plan_is_bounded():
     assert 0 < small < (256 << 20) and 0 < big < (256 << 20)
     # the workspace holds per-item counters plus partials sized by the grid, not by the prefixes
     assert F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 8, 4) == \
+        F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 64, 4)
+
+
+def test_attn_plan_fills_the_chip_at_full_size():
+    # Workspace = arrival counters (2 x 256 CUs x 4 waves ints) + partial O (2 slots per wave x
+    # rows x d f32) + partial max/sum (2 slots x 2 x rows f32), so it fixes the persistent grid:
+    # one 4-wave workgroup per CU with 16-row waves at the 256-request size, two per CU with
+    # shared 64-row items (the grid shrinks only for problems with few key tiles).
+    cnt = 2 * 256 * 4 * 4
+    W = 256 * 4
+    assert F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 64, 4) == \
+        cnt + 2 * W * 16 * 128 * 4 + 2 * W * 2 * 16 * 4
+    W = 2 * 256 * 4
+    assert F.attn_workspace_bytes(128, 64, 32, 8, 128, 64, 32, 16) == \
+        cnt + 2 * W * 16 * 128 * 4 + 2 * W * 2 * 16 * 4
+    # a tiny problem runs on a smaller grid: whole column groups on every XCD
+    assert F.attn_workspace_bytes(2, 16, 4, 4, 64, 16, 4, 4) < \
         F.attn_workspace_bytes(256, 32, 32, 8, 128, 64, 64, 4)
 
 
