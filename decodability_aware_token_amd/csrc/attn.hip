@@ -437,7 +437,9 @@ __device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, 
 // -inf, 0, 0, are never written out and weigh zero in a merge), and a group without rows
 // computes nothing: 16-token blocks, whose items mostly fill one of the four tiles, 171 -> 153
 // us.  With two the check measured slower (the pair's scores are issued together).
-template <int D, int QT, bool WO>
+// AHEAD (up to two query tiles): the next query tile's scores are issued before this one's
+// softmax; off where registers are short (shared tiles with two query tiles per wave).
+template <int D, int QT, bool WO, bool AHEAD = true>
 __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, int nq,
                                              const QOperand<D, QT>& qf,
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
@@ -485,7 +487,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, i
     const int cur = qt & 1;
     // up to two query tiles: the next tile's scores are issued ahead; with four the extra
     // registers would spill, so each tile's scores are computed at its turn
-    if (QT < 4 && qt + 1 < QT)
+    if (AHEAD && QT < 4 && qt + 1 < QT)
       tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
     if constexpr (kQAhead) {
       if (qt > 0) tile_scores_q<D>(T, qfr[cur], sc[cur][0], sc[cur][1]);
@@ -493,7 +495,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, i
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) qfr[cur ^ 1][kk] = qf.get(qt + 1, kk, lane);
       }
-    } else if (QT >= 4 && qt > 0) {
+    } else if ((QT >= 4 || !AHEAD) && qt > 0) {
       tile_scores<D, QT>(T, qf, qt, lane, sc[cur][0], sc[cur][1]);
     }
     float s[8];
@@ -814,7 +816,7 @@ __global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void att
     // (32-row tiles only: the 16-row kernel is held to 256 registers and its items are long,
     // and the 64-row kernels are short of registers; those merge piece by piece)
     constexpr int MM = kMaxMerge;
-    if (QT == 2 && npieces <= MM) {
+    if (QT == 2 && !SH && npieces <= MM) {
       int slot[MM];
       {
         int tp = c.start;
@@ -1001,8 +1003,9 @@ __global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void att
           read_tile<D, WO>(X, ring + (size_t)rb * CH, lane);
           const int ntp = C.ntp();
           const bool pg = C.tt < ntp;
-          compute_tile<D, QT, WO>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32, pg ? C.plen() : p.blk,
-                                  nq, qf, o, mrun, lrun, p.scale_log2, lane);
+          compute_tile<D, QT, WO, false>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32,
+                                         pg ? C.plen() : p.blk, nq, qf, o, mrun, lrun,
+                                         p.scale_log2, lane);
         }
         bad = bad || ((badbits >> rb) & 1);
         if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
@@ -1089,7 +1092,7 @@ hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
   size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
   if (QT >= 4) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
   if (SH) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kShBufs * 8 * D * 16;
-  constexpr int NB = SH ? kShPrefetch : (QT == 1 ? kPrefetchQt1 : 2);
+  constexpr int NB = SH ? (QT == 1 ? kShPrefetch : 1) : (QT == 1 ? kPrefetchQt1 : 2);
   hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH>), dim3(plan.wgs), dim3(256), shmem, s, prm,
                      prm.page_table);
   return hipGetLastError();
@@ -1103,20 +1106,21 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
   const int G = Hq / Hkv;
   const int rows = max_kept * G;
   const int cus = device_cus();
-  if (rows <= 32 || rows > 64) {
+  // shared tiles: 33..64 rows (16 per wave), and 65..128 rows with the output (32 per wave)
+  const bool shared = rows > 32 && (rows <= 64 || (rows <= 128 && !lse_only));
+  if (!shared) {
     // one wave per item: 16, 32 or 64 rows (several query groups per (request, kv head) past
-    // 64 rows).  Up to 32 rows, one 4-wave workgroup per CU (one wave per SIMD, each with NB
-    // tiles of 32 keys in flight); 64-row waves also one per CU with the output, while without
-    // it the larger query tiles are light enough for two workgroups per CU.
+    // 64 rows).  One 4-wave workgroup per CU (one wave per SIMD, each with NB tiles of 32 keys
+    // in flight); without the output the larger query tiles are light enough for two
+    // workgroups per CU, which hides their instruction latencies behind each other.
     pl.shared = false;
     pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
     pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
     pl.wgs = cus * ((pl.qt > 1 && lse_only) ? 2 : kWgsPerCuQt1);
   } else {
-    // 33..64 rows: shared tiles, 16 rows per wave, the four waves of a workgroup on one
-    // (request, kv head)'s tiles, two workgroups per CU
+    // the four waves of a workgroup on one (request, kv head)'s tiles, two workgroups per CU
     pl.shared = true;
-    pl.qt = 1;
+    pl.qt = rows <= 64 ? 1 : 2;
     pl.nqg = kWaves;
     pl.wgs = cus * kShWgsPerCu;
   }
@@ -1194,9 +1198,12 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
     if (plan.qt == 2) return launch_dq<128, 2, false>(prm, plan, s);
     return launch_dq<128, 4, false>(prm, plan, s);
   }
-  if (plan.shared)
+  if (plan.shared) {
+    if (plan.qt == 2) return a.d == 64 ? launch_dq<64, 2, true, true>(prm, plan, s)
+                                       : launch_dq<128, 2, true, true>(prm, plan, s);
     return a.d == 64 ? launch_dq<64, 1, true, true>(prm, plan, s)
                      : launch_dq<128, 1, true, true>(prm, plan, s);
+  }
   if (a.d == 64) {
     if (plan.qt == 1) return launch_dq<64, 1, true>(prm, plan, s);
     if (plan.qt == 2) return launch_dq<64, 2, true>(prm, plan, s);

@@ -297,6 +297,13 @@ ATTN_CASES = {
     # query groups per kv head, of which two, or one, hold rows (the others compute nothing)
     "g4_q64rows_bound_2_of_4_groups": ("sweep_b128_blk64", {"B": 6}, 20, 64),
     "g4_q64rows_bound_1_of_4_groups": ("sweep_b128_blk64", {"B": 6}, 12, 64),
+    # head dim 64 with shared tiles: 48 rows (16 per wave) and 96 rows (32 per wave)
+    "g4_d64_q48rows_shared": ("tiny_b2_blk16", {"B": 5, "blk": 32, "Hq": 8, "Hkv": 2, "S": 32,
+                                                "prefix": ("uniform", 1, 300),
+                                                "max_prefix": 320}, 12),
+    "g4_d64_q96rows_shared": ("tiny_b2_blk16", {"B": 5, "blk": 32, "Hq": 8, "Hkv": 2, "S": 32,
+                                                "prefix": ("uniform", 1, 300),
+                                                "max_prefix": 320}, 24),
 }
 
 
