@@ -14,7 +14,7 @@
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
-constexpr int kMaxB = 4096;
+constexpr int kMaxB = focus::kMaxB;
 constexpr int64_t kMaxRowBytes = int64_t(1) << 24;  // 16 MiB per gathered row
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
@@ -298,6 +298,10 @@ int front_end_prepare(const void* q0, const void* k0, const void* q1, const void
   const int64_t per_wg = 256 * 8 * 16;
   a.nsplit = (int)std::min<int64_t>(
       16, std::max<int64_t>(1, (max_kept * bytes + per_wg - 1) / per_wg));
+  // the score launch writes the offsets (from the masks and budgets), the second reads them
+  sa.scan_offsets = 1;
+  sa.sel = a.sel;
+  sa.offsets = offsets;
   return FOCUS_OK;
 }
 

@@ -8,6 +8,8 @@
 
 namespace focus {
 
+constexpr int kMaxB = 4096;  // largest batch of every call
+
 struct SelectArgs {
   const float* delta;
   const uint8_t* masked;
@@ -19,24 +21,6 @@ struct SelectArgs {
   uint8_t* keep;
   int32_t* kept_count;
 };
-struct ScoreArgs {
-  const void* q0;
-  const void* k0;
-  const void* q1;
-  const void* k1;
-  int is_bf16;
-  int B, blk, Hq, Hkv, d;
-  float scale_log2;  // sm_scale * log2(e)
-  const float* lse0; // [B, blk, Hq] full-domain row log-sum-exp of layer 0, or null (block-only)
-  const float* lse1; // same for layer 1
-  float* delta;      // [B, blk]
-  float* part;       // workspace [B, Hkv, blk]
-  int fuse_select;   // run the selection of each request right after its delta
-  SelectArgs sel;    // (delta unused: the request's delta is in registers)
-  int partial_only;  // stop after the per-kv-head partials (a later kernel reduces them)
-};
-size_t score_workspace_bytes(int B, int blk, int Hkv);
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
@@ -54,7 +38,8 @@ struct CompactArgs {
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
-// Reduction of the score partials + selection with caller budgets + compaction, one launch.
+// Reduction of the score partials + selection with caller budgets + compaction: the second
+// launch of the front end (the score launch has written the offsets).
 struct SelectCompactArgs {
   const float* part;  // [B, Hkv, blk] score partials
   int Hkv;
@@ -64,6 +49,29 @@ struct SelectCompactArgs {
   int nsplit;         // workgroups per request (each gathers a share of its rows), 1..16
 };
 hipError_t launch_select_compact(const SelectCompactArgs& a, hipStream_t s);
+
+struct ScoreArgs {
+  const void* q0;
+  const void* k0;
+  const void* q1;
+  const void* k1;
+  int is_bf16;
+  int B, blk, Hq, Hkv, d;
+  float scale_log2;  // sm_scale * log2(e)
+  const float* lse0; // [B, blk, Hq] full-domain row log-sum-exp of layer 0, or null (block-only)
+  const float* lse1; // same for layer 1
+  float* delta;      // [B, blk]
+  float* part;       // workspace [B, Hkv, blk]
+  int fuse_select;   // run the selection of each request right after its delta
+  SelectArgs sel;    // (delta unused: the request's delta is in registers)
+  int partial_only;  // stop after the per-kv-head partials (a later kernel reduces them)
+  // Front end with per-request budgets (block-only domain): the score launch also writes the
+  // compacted offsets from sel.masked and sel.budget, which launch_select_compact then reads.
+  int scan_offsets;
+  int32_t* offsets;  // [B+1]
+};
+size_t score_workspace_bytes(int B, int blk, int Hkv);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t* q;

@@ -11,11 +11,15 @@
 // local reduction plus two cross-lane steps, and the column sums accumulate in registers across
 // units and both layers (layer 0 subtracts, layer 1 adds).  The 16 query lanes are summed once
 // at the end, the 4 waves in LDS in a fixed order.  A second small kernel sums each request's
-// Hkv partials in kv-head order (deterministic, no atomics) and can run the request's selection
-// right away.
+// Hkv partials in kv-head order (deterministic, no float atomics) and can run the request's
+// selection right away.
+//
+// Front end with per-request budgets: workgroup 0 first scans the kept counts, known from the
+// masks and budgets alone, into the compacted offsets (O(B)), which the reduction + selection +
+// compaction kernel then reads.
 #include "device_common.h"
 #include "launch.h"
-#include "select_impl.h"
+#include "compact_impl.h"
 
 namespace focus {
 namespace {
@@ -160,7 +164,9 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
                                                             int Hkv, float scale_log2,
                                                             const float* __restrict__ lse0,
                                                             const float* __restrict__ lse1,
-                                                            float* __restrict__ part) {
+                                                            float* __restrict__ part,
+                                                            int scan_offsets, SelectArgs sel,
+                                                            int32_t* __restrict__ offsets) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int ROW = D + 16 / sizeof(T);
   constexpr int NMT = BLK / 16;
@@ -181,6 +187,17 @@ __global__ __launch_bounds__(256) void score_partial_kernel(const T* __restrict_
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) colacc[mt][i] = 0.f;
+
+  if constexpr (!FULL) {
+    if (scan_offsets && blockIdx.x == 0) {  // the scanning workgroup (LDS still free)
+      scan_kept(gridDim.x / Hkv, [&](int rr) { return budget_kept<BLK>(sel, rr); },
+                [&](int rr, int base, int k) {
+                  offsets[rr + 1] = base + k;
+                  if (rr == 0) offsets[0] = 0;
+                },
+                reinterpret_cast<int*>(smem));
+    }
+  }
 
   Pass<T, BLK, D, GS> ps;
   load_pass<T, BLK, D, GS>(ps, q0, k0, r, g, Hq, Hkv, G, 0, tid);
@@ -270,11 +287,12 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
   if (a.lse0 != nullptr)
     hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS, true>), dim3(a.B * a.Hkv), dim3(256),
                        shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1, (const T*)a.k1,
-                       a.Hq, a.Hkv, a.scale_log2, a.lse0, a.lse1, a.part);
+                       a.Hq, a.Hkv, a.scale_log2, a.lse0, a.lse1, a.part, 0, a.sel, nullptr);
   else
     hipLaunchKernelGGL((score_partial_kernel<T, BLK, D, GS, false>), dim3(a.B * a.Hkv),
                        dim3(256), shmem, s, (const T*)a.q0, (const T*)a.k0, (const T*)a.q1,
-                       (const T*)a.k1, a.Hq, a.Hkv, a.scale_log2, nullptr, nullptr, a.part);
+                       (const T*)a.k1, a.Hq, a.Hkv, a.scale_log2, nullptr, nullptr, a.part,
+                       a.scan_offsets, a.sel, a.offsets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial_only) return e;
   hipLaunchKernelGGL(score_reduce_kernel, dim3((a.B + 3) / 4), dim3(256), 0, s, a.part, a.B,

@@ -141,7 +141,8 @@ int focus_score_select(const void* q0, const void* k0, const void* q1, const voi
  *   gathered[n, :] = rows[r, kept_pos[n], :]   (byte copy of row_bytes bytes)
  * Entries n >= cap of kept_pos / gathered are not written; offsets always holds the true totals,
  * so offsets[B] > cap reveals an overflow after the caller synchronises.  cap >= B*blk always
- * suffices.
+ * suffices.  Two launches: one workgroup scans the kept counts into offsets (O(B)), then one
+ * workgroup per request writes its positions and gathers its rows.
  *
  *   keep        [B, blk] u8
  *   rows        [B, blk, row_bytes] bytes, or NULL (then gathered must be NULL: offsets only)
@@ -170,8 +171,9 @@ int focus_compact_multi(const uint8_t* keep, int B, int blk, int nsets, const vo
  * keep output: delta, keep, kept_count, offsets, kept_pos and the gathered rows.  With the
  * caller's integer budgets, request r keeps k_r = min(max(budget[r], 0), m_r) tokens, a number
  * known from the mask alone, so each request's place in the compacted order follows from the
- * masks and budgets of the requests before it: the second launch reduces the importance,
- * selects and gathers each request without waiting for the others.  (The adaptive rule needs
+ * masks and budgets of the requests before it: one workgroup of the scoring launch scans them
+ * into offsets (O(B)), and the second launch reduces the importance, selects and gathers each
+ * request without waiting for the others.  (The adaptive rule needs
  * every request's delta first: use focus_score_select and focus_compact_multi for it.)
  * Arguments, workspace and supported set: those of the two calls; masked must be 4-byte
  * aligned.  max_kept (1..blk) is the caller's bound of the kept counts: it sizes the launch

@@ -246,8 +246,11 @@ def test_compact_sentinel_rows_at_unkept_positions(nsets):
 # ------------------------------------------------------------------------------- compaction
 @pytest.mark.parametrize("blk,B,row_bytes,capfrac", [(16, 7, 16, 1.0), (32, 256, 8192, 1.0),
                                                      (64, 33, 96, 0.3), (32, 1, 256, 0.0),
-                                                     (64, 1500, 32, 1.0)])
+                                                     (64, 1500, 32, 1.0), (32, 2048, 48, 1.0),
+                                                     (16, 2049, 16, 0.5), (64, 4096, 32, 1.0)])
 def test_compact_isolated(blk, B, row_bytes, capfrac):
+    # up to 2048 requests every workgroup counts its predecessors' kept tokens; above, a
+    # one-workgroup scan of the kept counts runs first
     _announce(f"compact blk={blk} B={B} row_bytes={row_bytes} cap={capfrac}")
     rng = np.random.default_rng(blk * 1000 + B)
     keep = (rng.random((B, blk)) < 0.15).astype(np.uint8)
@@ -856,6 +859,8 @@ def test_fused_step_equals_separate_calls(name, over):
     ("sdar_b32_blk32", {"B": 40, "prefix": ("fixed", 64), "max_prefix": 64}, 0.05),  # overflow
     ("sweep_b128_blk16", {"B": 33, "prefix": ("fixed", 64), "max_prefix": 64}, 1.0),
     ("sweep_b128_blk64", {"B": 21, "prefix": ("fixed", 64), "max_prefix": 64}, 1.0),
+    ("tiny_b2_blk16", {"B": 4096}, 1.0),    # the largest batch: 16 requests per scan thread
+    ("tiny_b2_blk16", {"B": 2500}, 0.3),    # the compaction's scan launch, with overflow
 ])
 def test_score_select_compact_equals_two_calls(name, over, cap_frac):
     # the two-launch front end with per-request budgets (including budgets below zero and above
