@@ -362,7 +362,9 @@ size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, i
   if (B <= 0 || blk <= 0 || !group_ok(Hq, Hkv) || d <= 0 || S <= 0 || max_pages < 0 ||
       max_kept <= 0)
     return 0;
-  return focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept).ws_bytes;
+  // enough for the call with the output and for the log-sum-exp-only call
+  return std::max(focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept).ws_bytes,
+                  focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept, true).ws_bytes);
 }
 
 int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, const void* k_cache,

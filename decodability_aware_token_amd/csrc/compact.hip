@@ -110,6 +110,9 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectCompactArgs a
   __shared__ int s_k;
   const int tid = threadIdx.x, lane = tid & 63;
   const int r = blockIdx.x, split = blockIdx.y;
+  // every input first, so that their round trips overlap: the selection's mask byte and
+  // budget, the base offset, then the partials
+  const SelectInputs in = select_inputs(a.sel, r, lane);
   const int base = (tid == 0 && r > 0) ? a.cmp.offsets[r] : 0;
 
   // delta of position lane: the Hkv partials summed in kv-head order.  Eight partials are
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectCompactArgs a
       if (g0 + u < a.Hkv) dj += v[u];
   }
   if (lane >= BLK) dj = 0.f;
-  select_compact_request<BLK>(a, r, dj, split, gridDim.y, false, s_pos, s_wsum, &s_k,
+  select_compact_request<BLK>(a, r, dj, in, split, gridDim.y, false, s_pos, s_wsum, &s_k,
                               [&]() { return base; });
 }
 

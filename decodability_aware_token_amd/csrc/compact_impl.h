@@ -192,17 +192,18 @@ __device__ __forceinline__ void compact_finish(const CompactArgs& a, int r, bool
 }
 
 // Selection with the caller's budget and compaction of request r from its delta (dj: position
-// lane, 0 for lanes >= BLK), by a whole workgroup: every wave computes the selection (so no
-// barrier is needed before the gather), wave 0 of part 0 stores delta, keep and kept_count.
+// lane, 0 for lanes >= BLK) and its selection inputs already loaded, by a whole workgroup: every wave computes the selection (so no barrier is needed
+// before the gather), wave 0 of part 0 stores delta, keep and kept_count.
 // LDS: s_pos [64], s_wsum [4], s_k [1].
 template <int BLK, typename BaseFn>
 __device__ __forceinline__ void select_compact_request(const SelectCompactArgs& a, int r,
-                                                       float dj, int split, int nsplit,
-                                                       bool write_offsets, int* s_pos,
-                                                       int* s_wsum, int* s_k, BaseFn base) {
+                                                       float dj, SelectInputs in, int split,
+                                                       int nsplit, bool write_offsets,
+                                                       int* s_pos, int* s_wsum, int* s_k,
+                                                       BaseFn base) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const SelectArgs& sl = a.sel;
-  const Selection sel = select_compute(sl, r, dj, lane);
+  const Selection sel = select_decide(sl, in.m_byte, in.budget, dj, lane);
   const bool kj = sel.kept;
   const uint64_t bits = __ballot(kj);
   const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),

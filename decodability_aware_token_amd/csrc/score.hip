@@ -262,6 +262,8 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= B) return;  // uniform per wave
+  // the selection's inputs first, so that their round trip overlaps the partials'
+  const SelectInputs in = fuse_select ? select_inputs(sel, r, lane) : SelectInputs{0, 0};
   float sum = 0.f;
   if (lane < blk) {
     const float* pr = part + (size_t)r * Hkv * blk + lane;
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(const float* __restri
     }
     delta[(size_t)r * blk + lane] = sum;
   }
-  if (fuse_select) select_request(sel, r, sum, lane);
+  if (fuse_select) select_request(sel, r, in, sum, lane);
 }
 
 template <typename T, int BLK, int D, int GS>

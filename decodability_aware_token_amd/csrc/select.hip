@@ -13,8 +13,9 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= a.B) return;  // uniform per wave
+  const SelectInputs in = select_inputs(a, r, lane);
   const float dj = lane < a.blk ? a.delta[(size_t)r * a.blk + lane] : 0.f;
-  select_request(a, r, dj, lane);
+  select_request(a, r, in, dj, lane);
 }
 
 }  // namespace

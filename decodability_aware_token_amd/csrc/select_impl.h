@@ -32,13 +32,13 @@ struct Selection {
   int k;      // the request's kept count
 };
 
-// Every lane of the wave must call this (lanes >= blk pass any dj).  Reads the request's mask
-// (and budget) and returns the decision; stores nothing.
-__device__ __forceinline__ Selection select_compute(const SelectArgs& a, int r, float dj,
-                                                    int lane) {
+// The selection from inputs already loaded: mask byte m_byte of position lane (any value for
+// lanes >= blk) and the budget (ignored by the adaptive rule).  Every lane of the wave must
+// call this (lanes >= blk pass any dj); stores nothing.
+__device__ __forceinline__ Selection select_decide(const SelectArgs& a, uint8_t m_byte,
+                                                   int budget, float dj, int lane) {
   const int blk = a.blk;
-  const bool in_blk = lane < blk;
-  const bool mj = in_blk && a.masked[(size_t)r * blk + lane] != 0;
+  const bool mj = lane < blk && m_byte != 0;
   const uint64_t mbits = __ballot(mj);
   const int m = __popcll(mbits);
 
@@ -52,7 +52,7 @@ __device__ __forceinline__ Selection select_compute(const SelectArgs& a, int r, 
     const int c = m > 0 ? __popcll(__ballot(mj && dj > thr)) : 0;
     b = min(max(c, a.lo), a.hi);
   } else {
-    b = a.budget[r];
+    b = budget;
   }
   const int k = min(max(b, 0), m);
 
@@ -66,9 +66,21 @@ __device__ __forceinline__ Selection select_compute(const SelectArgs& a, int r, 
   return Selection{mj && rank < k, k};
 }
 
+// The request's mask byte of position lane and its budget (0 under the adaptive rule): loaded
+// before the deltas, so that their round trips overlap.
+struct SelectInputs {
+  uint8_t m_byte;
+  int budget;
+};
+__device__ __forceinline__ SelectInputs select_inputs(const SelectArgs& a, int r, int lane) {
+  return SelectInputs{a.masked[(size_t)r * a.blk + min(lane, a.blk - 1)],
+                      a.adaptive ? 0 : a.budget[r]};
+}
+
 // Every lane of the wave must call this (lanes >= blk pass any dj).
-__device__ __forceinline__ void select_request(const SelectArgs& a, int r, float dj, int lane) {
-  const Selection sel = select_compute(a, r, dj, lane);
+__device__ __forceinline__ void select_request(const SelectArgs& a, int r, SelectInputs in,
+                                               float dj, int lane) {
+  const Selection sel = select_decide(a, in.m_byte, in.budget, dj, lane);
   if (lane < a.blk) a.keep[(size_t)r * a.blk + lane] = sel.kept ? 1 : 0;
   if (lane == 0) a.kept_count[r] = sel.k;
 }
