@@ -49,7 +49,10 @@ constexpr int kWaves = 4;  // waves per workgroup
 constexpr int kPrefetchQt1 = 2;
 constexpr int kWgsPerCuQt1 = 1;
 // Shared tiles: tiles whose shares are in flight per workgroup, and workgroups per CU.
-constexpr int kShPrefetch = 2;
+// (Shared waves read a tile's key fragments from LDS, compute every query tile's scores, then
+// read the value fragments into the same registers: the two are never live together.)
+constexpr int kShPrefetch = 2;     // 16-row waves
+constexpr int kShPrefetchQt2 = 1;  // 32-row waves
 constexpr int kShWgsPerCu = 2;
 // cache-policy bits of a vector memory access with device scope (SC1): stores write through to
 // the device-coherent level, loads read from it (what device-scope atomics use on gfx950)
@@ -325,16 +328,21 @@ __device__ __forceinline__ void store_share(const Share<D>& sh, u32x4_t* buf, in
   }
 }
 
-// The wave's MFMA fragments of a tile from its LDS buffer: the registers load_tile fills.
-template <int D, bool WO>
-__device__ __forceinline__ void read_tile(Tile<D>& T, const u32x4_t* buf, int lane) {
-  constexpr int NK = D / 32, ND = D / 16;
+// The wave's MFMA fragments of a tile from its LDS buffer, the registers load_tile fills: the
+// key fragments (read_tile_k), the value fragments (read_tile_v).
+template <int D>
+__device__ __forceinline__ void read_tile_k(Tile<D>& T, const u32x4_t* buf, int lane) {
+  constexpr int NK = D / 32;
   const int m16 = lane & 15, j4 = lane >> 4;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) T.k[s][kk] = buf[(4 * kk + j4) * 32 + 16 * s + m16];
-  if constexpr (!WO) return;
+}
+template <int D>
+__device__ __forceinline__ void read_tile_v(Tile<D>& T, const u32x4_t* buf, int lane) {
+  constexpr int ND = D / 16;
+  const int m16 = lane & 15, j4 = lane >> 4;
   const u32x2_t* v8 = reinterpret_cast<const u32x2_t*>(buf + 4 * D);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) {
@@ -343,7 +351,6 @@ __device__ __forceinline__ void read_tile(Tile<D>& T, const u32x4_t* buf, int la
     T.v[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   }
 }
-
 // Workgroup barrier for the LDS tile ring: this wave's LDS writes are complete, and the
 // compiler moves no memory access across it (no wait on the vector memory loads in flight).
 __device__ __forceinline__ void lds_barrier() {
@@ -439,11 +446,15 @@ __device__ __forceinline__ void tile_scores(const Tile<D>& T, const QOperand<D, 
 // us.  With two the check measured slower (the pair's scores are issued together).
 // AHEAD (up to two query tiles): the next query tile's scores are issued before this one's
 // softmax; off where registers are short (shared tiles with two query tiles per wave).
-template <int D, int QT, bool WO, bool AHEAD = true>
+// SPLIT (shared tiles): T holds only the key fragments; the scores of every query tile are
+// computed first, then the value fragments are read from the LDS buffer vbuf into the same
+// registers, so keys and values are never live together.
+template <int D, int QT, bool WO, bool AHEAD = true, bool SPLIT = false>
 __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, int nq,
                                              const QOperand<D, QT>& qf,
                                              f32x4_t (&o)[QT][D / 16], float (&mrun)[QT],
-                                             float (&lrun)[QT], float scale_log2, int lane) {
+                                             float (&lrun)[QT], float scale_log2, int lane,
+                                             const u32x4_t* vbuf = nullptr) {
   constexpr int ND = D / 16;
   if (QT > 2 && nq <= 0) return;
   const int j4 = lane >> 4;
@@ -451,7 +462,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, i
   // key0 + 16 + 4j + (0..3); nv[r] = valid keys of run r
   const int nv[2] = {nvalid - (key0 + 4 * j4), nvalid - (key0 + 16 + 4 * j4)};
   const bool full = key0 + 32 <= nvalid;  // wave-uniform: only the last tile of a range is short
-  if (WO && !full) {
+  auto mask_values = [&]() {
     // Values of keys past the end are zeroed: their weights are zero, but the loaded values
     // may be anything and 0 * NaN would not vanish.
     u32x4_t vmask;
@@ -462,6 +473,18 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, i
     }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) T.v[dt] &= vmask;
+  };
+  f32x4_t scs[SPLIT ? QT : 1][2];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) tile_scores<D, QT>(T, qf, qt, lane, scs[qt][0], scs[qt][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (WO) {
+      read_tile_v<D>(T, vbuf, lane);
+      if (!full) mask_values();
+    }
+  } else if (WO && !full) {
+    mask_values();
   }
   const float inv_scale = 1.f / scale_log2;
   f32x4_t sc[2][2];
@@ -471,7 +494,8 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, i
   constexpr int NK = D / 32;
   constexpr bool kQAhead = QT >= 4 && !WO;
   u32x4_t qfr[2][NK];  // fragments of the query tiles of parity 0 and 1
-  if constexpr (kQAhead) {
+  if constexpr (SPLIT) {
+  } else if constexpr (kQAhead) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qfr[0][kk] = qf.get(0, kk, lane);
     tile_scores_q<D>(T, qfr[0], sc[0][0], sc[0][1]);
@@ -487,9 +511,12 @@ __device__ __forceinline__ void compute_tile(Tile<D>& T, int key0, int nvalid, i
     const int cur = qt & 1;
     // up to two query tiles: the next tile's scores are issued ahead; with four the extra
     // registers would spill, so each tile's scores are computed at its turn
-    if (AHEAD && QT < 4 && qt + 1 < QT)
+    if (!SPLIT && AHEAD && QT < 4 && qt + 1 < QT)
       tile_scores<D, QT>(T, qf, qt + 1, lane, sc[cur ^ 1][0], sc[cur ^ 1][1]);
-    if constexpr (kQAhead) {
+    if constexpr (SPLIT) {
+      sc[cur][0] = scs[qt][0];
+      sc[cur][1] = scs[qt][1];
+    } else if constexpr (kQAhead) {
       if (qt > 0) tile_scores_q<D>(T, qfr[cur], sc[cur][0], sc[cur][1]);
       if (qt + 1 < QT && qt + 1 < nq) {
 #pragma unroll
@@ -1000,12 +1027,12 @@ __global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void att
         const int nq = (C.nrows - C.qg * R + 15) >> 4;
         if (nq > 0) {
           Tile<D> X;
-          read_tile<D, WO>(X, ring + (size_t)rb * CH, lane);
           const int ntp = C.ntp();
           const bool pg = C.tt < ntp;
-          compute_tile<D, QT, WO, false>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32,
-                                         pg ? C.plen() : p.blk, nq, qf, o, mrun, lrun,
-                                         p.scale_log2, lane);
+          read_tile_k<D>(X, ring + (size_t)rb * CH, lane);
+          compute_tile<D, QT, WO, false, true>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32,
+                                               pg ? C.plen() : p.blk, nq, qf, o, mrun, lrun,
+                                               p.scale_log2, lane, ring + (size_t)rb * CH);
         }
         bad = bad || ((badbits >> rb) & 1);
         if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
@@ -1092,7 +1119,7 @@ hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
   size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
   if (QT >= 4) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
   if (SH) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kShBufs * 8 * D * 16;
-  constexpr int NB = SH ? (QT == 1 ? kShPrefetch : 1) : (QT == 1 ? kPrefetchQt1 : 2);
+  constexpr int NB = SH ? (QT == 1 ? kShPrefetch : kShPrefetchQt2) : (QT == 1 ? kPrefetchQt1 : 2);
   hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH>), dim3(plan.wgs), dim3(256), shmem, s, prm,
                      prm.page_table);
   return hipGetLastError();
