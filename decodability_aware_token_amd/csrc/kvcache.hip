@@ -16,18 +16,46 @@ constexpr int kBatch = 8;  // 16-byte chunks per thread with their loads in flig
 constexpr int kWritebackSplit = 2;  // workgroups per request in the write-back
 
 // kWritebackSplit workgroups per request, each moving its share of the request's kept rows' fresh
-// K/V into the block KV at their positions.  Loads of a batch are all issued before its stores
-// (source and destination may alias as far as the compiler knows, so a load after a store would
-// wait for it).
+// K/V into the block KV at their positions.  First the request's positions are mapped to the
+// rows that write them in LDS (a position named by several rows takes the last of them, as a
+// sequential write would, so every destination is written once), then:
+//  * keys: one 16-byte chunk per (position, head, 8-dim group), a whole run of 8 dims;
+//  * values: one 2-byte element per (position, head, dim): the V layout interleaves 8 positions
+//    per 16-byte chunk.  (Rebuilding each touched chunk whole -- the cached chunk merged with
+//    the written values, one 16-byte store -- measured slower: its extra loads cost more than
+//    the stores it saves.)
+// Loads of a batch are all issued before its stores (source and destination may alias as far
+// as the compiler knows, so a load after a store would wait for it).
 __global__ __launch_bounds__(256) void kv_writeback_kernel(WritebackArgs a) {
-  const int r = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  __shared__ int s_row[64];  // position -> row writing it, -1 if none
+  __shared__ int s_pos[64];  // positions with a row, ascending
+  __shared__ int s_np;
+  const int r = blockIdx.x, split = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int n0 = a.offsets[r];
   const int n1 = min(a.offsets[r + 1], a.cap);
   const int nrows = min(n1 - n0, a.blk);  // a request keeps at most blk rows
   if (n0 < 0 || nrows <= 0) return;
+  if (tid < 64) s_row[tid] = -1;
+  __syncthreads();
+  if (tid < nrows) {
+    const int j = a.kept_pos[n0 + tid];
+    // invalid device data (a position outside the block): the row is skipped
+    if (j >= 0 && j < a.blk) atomicMax(&s_row[j], n0 + tid);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const bool has = lane < a.blk && s_row[lane] >= 0;
+    const uint64_t m = __ballot(has);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (has) s_pos[rank] = lane;
+    if (lane == 0) s_np = __popcll(m);
+  }
+  __syncthreads();
+  const int np = s_np;
   const int D8 = a.d / 8;
-  // keys: one 16-byte chunk per (row, head, 8-dim group)
-  const int kchunks = nrows * a.Hkv * D8;
+  // keys
+  const int kchunks = np * a.Hkv * D8;
   const int kper = (kchunks + gridDim.y - 1) / gridDim.y;
   const int k_lo = split * kper, k_hi = min(k_lo + kper, kchunks);
   for (int c0 = k_lo + tid; c0 < k_hi; c0 += 256 * kBatch) {
@@ -36,20 +64,18 @@ __global__ __launch_bounds__(256) void kv_writeback_kernel(WritebackArgs a) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int c = min(c0 + 256 * u, k_hi - 1);
-      const int n = n0 + c / (a.Hkv * D8), rem = c % (a.Hkv * D8);
+      const int q = c / (a.Hkv * D8), rem = c % (a.Hkv * D8);
       const int g = rem / D8, c8 = rem % D8;
-      const int j = a.kept_pos[n];
+      const int j = s_pos[q], n = s_row[j];
       v[u] = load16(a.k_rows + ((size_t)n * a.Hkv + g) * a.d + 8 * c8);
-      // invalid device data (a position outside the block): the row is skipped
-      dst[u] = (j >= 0 && j < a.blk && c0 + 256 * u < k_hi)
-                   ? ((((int64_t)r * a.Hkv + g) * D8 + c8) * a.blk + j) : -1;
+      dst[u] = c0 + 256 * u < k_hi ? ((((int64_t)r * a.Hkv + g) * D8 + c8) * a.blk + j) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
       if (dst[u] >= 0) *reinterpret_cast<uint4*>(a.k_blk + dst[u] * 8) = v[u];
   }
-  // values: one 2-byte element per (row, head, dim)
-  const int velems = nrows * a.Hkv * a.d;
+  // values: one 2-byte element per (written position, head, dim)
+  const int velems = np * a.Hkv * a.d;
   const int vper = (velems + gridDim.y - 1) / gridDim.y;
   const int v_lo = split * vper, v_hi = min(v_lo + vper, velems);
   for (int e0 = v_lo + tid; e0 < v_hi; e0 += 256 * kBatch) {
@@ -58,11 +84,11 @@ __global__ __launch_bounds__(256) void kv_writeback_kernel(WritebackArgs a) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int e = min(e0 + 256 * u, v_hi - 1);
-      const int n = n0 + e / (a.Hkv * a.d), rem = e % (a.Hkv * a.d);
+      const int q = e / (a.Hkv * a.d), rem = e % (a.Hkv * a.d);
       const int g = rem / a.d, c = rem % a.d;
-      const int j = a.kept_pos[n];
+      const int j = s_pos[q], n = s_row[j];
       v[u] = a.v_rows[((size_t)n * a.Hkv + g) * a.d + c];
-      dst[u] = (j >= 0 && j < a.blk && e0 + 256 * u < v_hi)
+      dst[u] = e0 + 256 * u < v_hi
                    ? ((((int64_t)r * a.Hkv + g) * (a.blk / 8) + j / 8) * a.d + c) * 8 + j % 8
                    : -1;
     }

@@ -274,7 +274,8 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
  *   k_rows, v_rows  [cap, Hkv, d] bf16 (compacted order, e.g. from the gathered hidden rows)
  *   offsets [B+1], kept_pos [cap] i32 (as produced by focus_compact)
  *   k_blk [B, Hkv, d/8, blk, 8], v_blk [B, Hkv, blk/8, d, 8] bf16, updated in place
- * A row whose kept_pos is outside [0, blk) is skipped; at most blk rows of a request are read.
+ * A row whose kept_pos is outside [0, blk) is skipped; at most blk rows of a request are read;
+ * a position named by several rows of a request takes the last of those rows.
  * Supported: blk in {16,32,64}; d in {64,128}; Hkv <= 64; 1 <= B <= 4096; K/V pointers 16-byte
  * aligned.  cap == 0 does nothing.
  * ------------------------------------------------------------------------------------------ */

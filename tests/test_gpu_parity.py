@@ -737,6 +737,33 @@ def test_kv_writeback(name, over):
     assert np.array_equal(_bits(kb), ref_k) and np.array_equal(_bits(vb), ref_v)
 
 
+def test_kv_writeback_repeated_and_invalid_positions():
+    # a position named by several rows of a request takes the last of them (as the oracle's
+    # row-order writes do); rows whose position is outside the block are skipped, so the
+    # reference is the oracle on the other rows.  Request 1 writes a whole 8-position group.
+    from workloads import f32_to_bf16_bits
+    _announce("kv writeback repeated / invalid positions")
+    rng = np.random.default_rng(43)
+    B, blk, Hkv, d = 3, 32, 2, 64
+    pos = [[3, 7, 3, 40, -1, 31, 7], list(range(8, 16)) + [20], []]
+    offsets = np.concatenate([[0], np.cumsum([len(x) for x in pos])]).astype(np.int32)
+    kept_pos = np.array(sum(pos, []), dtype=np.int32)
+    T = int(offsets[-1])
+    k_rows = f32_to_bf16_bits(rng.standard_normal((T, Hkv, d)).astype(np.float32))
+    v_rows = f32_to_bf16_bits(rng.standard_normal((T, Hkv, d)).astype(np.float32))
+    k_blk = f32_to_bf16_bits(rng.standard_normal((B, Hkv, d // 8, blk, 8)).astype(np.float32))
+    v_blk = f32_to_bf16_bits(rng.standard_normal((B, Hkv, blk // 8, d, 8)).astype(np.float32))
+    ok = (kept_pos >= 0) & (kept_pos < blk)
+    owner = np.repeat(np.arange(B), np.diff(offsets))
+    ref_off = np.concatenate([[0], np.cumsum(np.bincount(owner[ok], minlength=B))])
+    ref_k, ref_v = O.kv_writeback(k_rows[ok], v_rows[ok], ref_off, kept_pos[ok], k_blk, v_blk)
+    kb, vb = bf16_tensor(k_blk, DEV), bf16_tensor(v_blk, DEV)
+    F.kv_writeback(bf16_tensor(k_rows, DEV), bf16_tensor(v_rows, DEV),
+                   torch.from_numpy(offsets).to(DEV), torch.from_numpy(kept_pos).to(DEV), kb, vb)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(kb), ref_k) and np.array_equal(_bits(vb), ref_v)
+
+
 def _commit_case(st, rng, nfree, commit, shuffle=True):
     """Device state for a commit: the step's caches plus nfree free pages (the stack)."""
     pool = st.k_cache.shape[0]
