@@ -307,6 +307,13 @@ ATTN_CASES = {
     "g4_d64_q96rows_shared": ("tiny_b2_blk16", {"B": 5, "blk": 32, "Hq": 8, "Hkv": 2, "S": 32,
                                                 "prefix": ("uniform", 1, 300),
                                                 "max_prefix": 320}, 24),
+    # the largest batches: 16 requests per thread in every workgroup's metadata scan and the
+    # widest search rounds; one wave per item, and shared tiles with 4096 requests' metadata
+    # beside the tile ring in LDS
+    "g1_d64_b4096": ("tiny_b2_blk16", {"B": 4096, "prefix": ("uniform", 0, 64)}, 4),
+    "g4_d64_b2500_shared": ("tiny_b2_blk16", {"B": 2500, "blk": 32, "Hq": 8, "Hkv": 2, "S": 32,
+                                              "prefix": ("uniform", 1, 100),
+                                              "max_prefix": 128}, 12),
 }
 
 
