@@ -10,8 +10,9 @@
 // streamed as 32-key tiles (columns), the prefix tiles first, then the block tiles.  The columns
 // of all requests form one global list.
 //
-// Column groups.  The grid is persistent, one 4-wave workgroup per CU, its waves in groups of
-// Hkv*nqg, one wave per (kv head, query group).  Group i takes the i-th of equal contiguous slices
+// Column groups.  The grid is persistent, one 4-wave workgroup per CU (two for shared tiles and
+// for the 32- and 64-row tiles without the output), its waves in groups of Hkv*nqg, one wave per
+// (kv head, query group).  Group i takes the i-th of equal contiguous slices
 // of the column list, so the waves of a group stream the same pages of the same requests at the
 // same time, each its own kv head's part of the page: every page is read by all its heads
 // together, which keeps the DRAM accesses local wherever the slices fall.  A wave streams its
@@ -33,6 +34,11 @@
 //   * V pages [page, Hkv, S/8, d, 8]: a lane's two 8-byte loads are one dim of the two 4-key
 //     runs its S^T lane group holds, which is exactly the A operand of O^T = V^T P^T for that
 //     lane group; P^T (bf16) comes straight from the S^T registers.
+// Shared tiles.  Items of 33..64 rows, and of 65..128 rows with the output, take all four waves
+// of a workgroup, one 16- or 32-row query group each, on the same kv head: the workgroup loads
+// each tile once (every thread a 1/256 share into registers, written to a ring of three LDS tile
+// buffers, one barrier per tile), and each wave reads the MFMA fragments above from LDS -- the
+// keys, then, after its scores, the values into the same registers.
 // Softmax is online in the exp2 domain (f32).  Merges run in a fixed order, so results are
 // bitwise reproducible.
 #include "device_common.h"
