@@ -54,11 +54,20 @@ def score_algorithmic(st):
     return by, fl
 
 
+def code_only(text):
+    """Source text without its comments and blank space: what a comment edit leaves unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
+    """Hash of the attention kernel's code (comments and spacing excluded)."""
     h = hashlib.sha256()
     for f in ("attn.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "decodability_aware_token_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decodability_aware_token_amd", "csrc", f)) as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
