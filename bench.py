@@ -416,6 +416,49 @@ class Flush:
             torch.sum(self.buf, dim=0, out=self.out)
 
 
+def front_end_batch(args):
+    """The front end alone at batch args.front_end_batch with the workload's shapes: layer-0/1
+    Q/K, hidden states and attention queries drawn on the device from a seeded generator, each
+    position masked with probability 0.8, the budget ceil(0.125 * masked count) (the headline's
+    rule).  Prints one JSON line: mean us per call (caches flushed before each) and the score
+    inputs' bytes."""
+    import torch
+    from decodability_aware_token_amd import binding as F
+    from workloads import BY_NAME
+    rc = BY_NAME[args.workload]
+    B, blk, Hq, Hkv, d = args.front_end_batch, rc.blk, rc.Hq, rc.Hkv, rc.d
+    W = rc.hidden or Hq * d
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(rc.seed)
+    draw = lambda *shape: (torch.randn(*shape, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+    q0, q1 = draw(B, blk, Hq, d), draw(B, blk, Hq, d)
+    k0, k1 = draw(B, blk, Hkv, d), draw(B, blk, Hkv, d)
+    masked = (torch.rand(B, blk, device=dev, generator=g) < 0.8).to(torch.uint8)
+    budget = torch.ceil(0.125 * masked.sum(1).float()).to(torch.int32)
+    sets = [draw(B, blk, W), draw(B, blk, Hq, d)]
+    cap = B * blk
+    outs = dict(delta=torch.empty(B, blk, device=dev),
+                keep=torch.empty(B, blk, dtype=torch.uint8, device=dev),
+                kept_count=torch.empty(B, dtype=torch.int32, device=dev),
+                offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
+                kept_pos=torch.empty(cap, dtype=torch.int32, device=dev),
+                gathered=[torch.empty((cap,) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+                          for x in sets])
+    ws = torch.zeros(F.lib().focus_score_l01_workspace_size(B, blk, Hq, Hkv, d),
+                     dtype=torch.uint8, device=dev)
+    max_kept = -(-blk // 8)
+    fn = lambda: F.score_select_compact(q0, k0, q1, k1, d ** -0.5, masked, budget, sets, cap,
+                                        max_kept=max_kept, workspace=ws, **outs)
+    for _ in range(args.warmup):
+        fn()
+    ms = timed(fn, args.steps, Flush(dev, enabled=not args.no_flush),
+               torch.cuda.current_stream(dev))
+    print(json.dumps({"front_end_batch": B, "workload_shapes": rc.name, "us": round(ms * 1e3, 2),
+                      "kept_tokens": int(outs["offsets"][-1]),
+                      "score_input_bytes": 2 * B * blk * (Hq + Hkv) * d * 2}))
+
+
 def timed(fn, steps, flush, stream):
     """Mean ms of fn() over `steps` calls, each bracketed by HIP events on `stream` with a cache
     flush before it (outside the events)."""
@@ -546,6 +589,10 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes) 5 times, "
                          "to scale HBM byte counters")
+    ap.add_argument("--front-end-batch", type=int, metavar="B",
+                    help="only time the front end (score + select + compact of the hidden states "
+                         "and queries) at batch B with --workload's shapes, on seeded synthetic "
+                         "device tensors (no attention inputs are generated)")
     ap.add_argument("--oracle-worker", nargs=5, metavar=("RECIPE", "B", "SEED", "STRIDE", "S"),
                     help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -580,6 +627,9 @@ def main():
         ms = e0.elapsed_time(e1) / 5
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "ms": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
+        return
+    if args.front_end_batch:
+        front_end_batch(args)
         return
     from decodability_aware_token_amd import FocusStep, StepInputs
     from workloads import BY_NAME, make_step
