@@ -57,7 +57,7 @@ constexpr int kWgsPerCuQt1 = 1;
 // Shared tiles: tiles whose shares are in flight per workgroup, and workgroups per CU.
 // (Shared waves read a tile's key fragments from LDS, compute every query tile's scores, then
 // read the value fragments into the same registers: the two are never live together.)
-constexpr int kShPrefetch = 2;     // 16-row waves
+constexpr int kShPrefetch = 3;     // 16-row waves
 constexpr int kShPrefetchQt2 = 1;  // 32-row waves
 constexpr int kShWgsPerCu = 2;
 // cache-policy bits of a vector memory access with device scope (SC1): stores write through to
