@@ -301,11 +301,11 @@ def focused_attn_kernel(recipe):
     """Name of the attention instantiation the focused step of a recipe launches, as the launch
     plan chooses it: <d, query tiles per wave, tiles in flight, output, shared tiles>.  Items of
     33..128 rows share each tile among a workgroup's four waves (16 rows per wave up to 64, 32
-    rows with one share in flight above); the others run one wave per item."""
+    rows with one share in flight above, three below); the others run one wave per item."""
     rows = recipe.max_kept() * recipe.G
     if 32 < rows <= 128:
         qt = 1 if rows <= 64 else 2
-        return f"attn_kernel<{recipe.d}, {qt}, {2 if qt == 1 else 1}, true, true>"
+        return f"attn_kernel<{recipe.d}, {qt}, {3 if qt == 1 else 1}, true, true>"
     qt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
     return f"attn_kernel<{recipe.d}, {qt}, 2, true, false>"
 

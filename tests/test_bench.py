@@ -98,8 +98,8 @@ def test_focused_attention_instantiation_per_recipe():
                 "longctx_b64_blk32": "attn_kernel<128, 1, 2, true, false>",
                 "tiny_b2_blk16": "attn_kernel<64, 1, 2, true, false>"}
     # the adaptive recipes' launch bound is 16 kept tokens x 4 query heads = 64 rows: shared
-    shared = {"sweep_b128_blk64": "attn_kernel<128, 1, 2, true, true>",
-              "sweep_b128_blk16": "attn_kernel<128, 1, 2, true, true>"}
+    shared = {"sweep_b128_blk64": "attn_kernel<128, 1, 3, true, true>",
+              "sweep_b128_blk16": "attn_kernel<128, 1, 3, true, true>"}
     for name, want in {**one_wave, **shared}.items():
         assert bench.focused_attn_kernel(BY_NAME[name]) == want, name
 
