@@ -141,8 +141,9 @@ int focus_score_select(const void* q0, const void* k0, const void* q1, const voi
  *   gathered[n, :] = rows[r, kept_pos[n], :]   (byte copy of row_bytes bytes)
  * Entries n >= cap of kept_pos / gathered are not written; offsets always holds the true totals,
  * so offsets[B] > cap reveals an overflow after the caller synchronises.  cap >= B*blk always
- * suffices.  Two launches: one workgroup scans the kept counts into offsets (O(B)), then one
- * workgroup per request writes its positions and gathers its rows.
+ * suffices.  One workgroup per request writes its positions and gathers its rows; its place in
+ * the order is counted by the workgroup itself up to 2048 requests, and above that by a first
+ * launch, one workgroup scanning the kept counts into offsets (O(B)).
  *
  *   keep        [B, blk] u8
  *   rows        [B, blk, row_bytes] bytes, or NULL (then gathered must be NULL: offsets only)
