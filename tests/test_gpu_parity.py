@@ -307,6 +307,13 @@ ATTN_CASES = {
     "g4_d64_q96rows_shared": ("tiny_b2_blk16", {"B": 5, "blk": 32, "Hq": 8, "Hkv": 2, "S": 32,
                                                 "prefix": ("uniform", 1, 300),
                                                 "max_prefix": 320}, 24),
+    # shared 16-row waves over 16-token pages: a 32-key tile spans two pages, each thread's
+    # share taking its keys and values from either
+    "g4_d128_s16_q48rows_shared": ("longctx_b64_blk32", {"B": 4, "prefix": ("uniform", 1, 700),
+                                                         "max_prefix": 800}, 12),
+    "g4_d64_s16_q48rows_shared": ("tiny_b2_blk16", {"B": 5, "blk": 32, "Hq": 8, "Hkv": 2,
+                                                    "prefix": ("uniform", 1, 300),
+                                                    "max_prefix": 320}, 12),
     # the largest batches: 16 requests per thread in every workgroup's metadata scan and the
     # widest search rounds; one wave per item, and shared tiles with 4096 requests' metadata
     # beside the tile ring in LDS
