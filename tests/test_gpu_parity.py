@@ -433,21 +433,24 @@ def test_attn_poisoned_unused_memory_is_never_read():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
-def test_attn_invalid_device_data_gives_nan_rows():
-    _announce("attn invalid page id / prefix length")
+@pytest.mark.parametrize("max_kept", [4, 12, 24])
+def test_attn_invalid_device_data_gives_nan_rows(max_kept):
+    # 4 kept tokens x G = 4: one wave per item; 12 and 24: shared tiles with 16- and 32-row
+    # waves, where the invalid page id is seen by one thread's share and must reach every wave
+    _announce(f"attn invalid page id / prefix length, max_kept={max_kept}")
     st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=6))
-    keep = _random_keep(np.random.default_rng(9), st.B, st.blk, 4, empty_frac=0.0)
+    keep = _random_keep(np.random.default_rng(9), st.B, st.blk, max_kept, empty_frac=0.0)
     c = attn_case_inputs(st, keep)
     t = step_inputs(st)
     ref, ref_lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache,
-                                       t.page_table, t.prefix_len, t.k_blk, t.v_blk, 4,
+                                       t.page_table, t.prefix_len, t.k_blk, t.v_blk, max_kept,
                                        st.sm_scale)
     pt = t.page_table.clone()
     pt[1, 0] = st.num_pages + 5          # request 1: a used page id out of range
     pl = t.prefix_len.clone()
     pl[3] = -4                           # request 3: negative prefix length
     out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache, pt, pl,
-                                   t.k_blk, t.v_blk, 4, st.sm_scale)
+                                   t.k_blk, t.v_blk, max_kept, st.sm_scale)
     torch.cuda.synchronize()
     off = c["offsets"]
     for r in range(st.B):
