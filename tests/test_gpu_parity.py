@@ -412,20 +412,22 @@ def test_attn_growing_logits_rescale():
     assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
 
 
-def test_attn_poisoned_unused_memory_is_never_read():
+@pytest.mark.parametrize("max_kept", [4, 12, 24])
+def test_attn_poisoned_unused_memory_is_never_read(max_kept):
     # NaN in every cache slot past a prefix and in spare pages, out-of-range ids past each
-    # request's last page: the result must equal the clean run bit for bit
-    _announce("attn poison")
+    # request's last page: the result must equal the clean run bit for bit (one wave per item,
+    # and shared tiles with 16- and 32-row waves over 16-token pages)
+    _announce(f"attn poison, max_kept={max_kept}")
     rec = BY_NAME["longctx_b64_blk32"].scaled(B=4)
     clean = make_step(rec)
     pois = make_step(rec, poison=True)
-    keep = _random_keep(np.random.default_rng(5), rec.B, rec.blk, 4, empty_frac=0.0)
+    keep = _random_keep(np.random.default_rng(5), rec.B, rec.blk, max_kept, empty_frac=0.0)
     outs = []
     for st in (clean, pois):
         c = attn_case_inputs(st, keep)
         t = step_inputs(st)
         out, lse = F.ragged_paged_attn(c["d_q"], c["d_offsets"], t.k_cache, t.v_cache,
-                                       t.page_table, t.prefix_len, t.k_blk, t.v_blk, 4,
+                                       t.page_table, t.prefix_len, t.k_blk, t.v_blk, max_kept,
                                        st.sm_scale)
         torch.cuda.synchronize()
         outs.append((bf16_to_np(out), lse.cpu().numpy()))
