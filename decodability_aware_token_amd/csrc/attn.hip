@@ -11,7 +11,8 @@
 // of all requests form one global list.
 //
 // Column groups.  The grid is persistent, one 4-wave workgroup per CU (two for shared tiles and
-// for the 32- and 64-row tiles without the output), its waves in groups of Hkv*nqg, one wave per
+// for the 32- and 64-row tiles without the output, as far as the LDS holds them all at once:
+// the staged metadata grows with the batch), its waves in groups of Hkv*nqg, one wave per
 // (kv head, query group).  Group i takes the i-th of equal contiguous slices
 // of the column list, so the waves of a group stream the same pages of the same requests at the
 // same time, each its own kv head's part of the page: every page is read by all its heads
@@ -36,11 +37,13 @@
 //     lane group; P^T (bf16) comes straight from the S^T registers.
 // Shared tiles.  Items of 33..64 rows, and of 65..128 rows with the output, take all four waves
 // of a workgroup, one 16- or 32-row query group each, on the same kv head: the workgroup loads
-// each tile once (every thread a 1/256 share into registers, written to a ring of three LDS tile
-// buffers, one barrier per tile), and each wave reads the MFMA fragments above from LDS -- the
-// keys, then, after its scores, the values into the same registers.
+// each tile once (every thread loads a 1/256 share straight into a ring of four LDS tile buffers,
+// three tiles ahead, one barrier per tile), and each wave reads the MFMA fragments above from
+// LDS -- the keys, then, after its scores, the values into the same registers.
 // Softmax is online in the exp2 domain (f32).  Merges run in a fixed order, so results are
 // bitwise reproducible.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -54,12 +57,18 @@ constexpr int kWaves = 4;  // waves per workgroup
 // accesses more local, and the CU's outstanding misses are the limit, not the wave count.
 constexpr int kPrefetchQt1 = 2;
 constexpr int kWgsPerCuQt1 = 1;
-// Shared tiles: tiles whose shares are in flight per workgroup, and workgroups per CU.
-// (Shared waves read a tile's key fragments from LDS, compute every query tile's scores, then
-// read the value fragments into the same registers: the two are never live together.)
+// Shared tiles: tiles on their way into LDS per workgroup (ahead of the one computed), and
+// workgroups per CU.  (Shared waves read a tile's key fragments from LDS, compute every query
+// tile's scores, then read the value fragments into the same registers: the two are never live
+// together.)
 constexpr int kShPrefetch = 3;     // 16-row waves
-constexpr int kShPrefetchQt2 = 1;  // 32-row waves
-constexpr int kShWgsPerCu = 2;
+constexpr int kShPrefetchQt2 = 3;  // 32-row waves
+constexpr int kShWgsPerCu = 2;     // 32-row waves
+constexpr int kShWgsPerCuQt1 = 2;  // 16-row waves
+// LDS per CU (gfx950); the planner caps the workgroups per CU so that they are all resident
+constexpr size_t kLdsPerCu = 160 * 1024;
+// the most workgroups per CU of any mode (the log-sum-exp-only one-wave kernels take two)
+constexpr int kMaxWgsPerCu = std::max({2, kWgsPerCuQt1, kShWgsPerCu, kShWgsPerCuQt1});
 // cache-policy bits of a vector memory access with device scope (SC1): stores write through to
 // the device-coherent level, loads read from it (what device-scope atomics use on gfx950)
 constexpr int kCpolDevice = 16;
@@ -252,25 +261,35 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const Cursor& c, Pages pg,
 // Shared tiles.  When an item's rows need several query groups, the four waves of a workgroup
 // are four query groups of the same kv head: they stream the same tiles, so the workgroup loads
 // each tile once.  Every thread loads a 1/256 share of a tile (D/64 chunks of 16 bytes of K and
-// as many of V) into registers NB tiles ahead of use; the shares pass through a ring of three
-// LDS tile buffers, one barrier per tile, and each wave reads its MFMA fragments from LDS.
+// as many of V) straight into an LDS tile buffer (no registers), NB tiles ahead of use; one
+// barrier per tile, and each wave reads its MFMA fragments from LDS.
 // Tile buffer layout (16-byte chunks): K chunk (dim group c, key k) at c*32 + k, then V chunk
 // (key group q, dim e) at 4*D + q*D + e -- the global layouts restricted to the tile's 32 keys.
-constexpr int kShBufs = 3;
+// Thread t's chunk u is chunk 256u + t, so each wave's loads fill 64 consecutive chunks.
 
-template <int D>
-struct Share {
-  static constexpr int NC = D / 64;  // 16-byte chunks of K, and of V, per thread
-  u32x4_t k[NC], v[NC];
-  bool bad;  // a page id of the tile was out of range (page 0 was read instead)
-};
+// cache-policy bits of a load of data read exactly once (non-temporal)
+constexpr int kCpolNontemporal = 2;
 
-// This thread's share of the cursor's tile, branch-free and clamped like load_tile: K chunks
-// of keys past the valid length hold the last valid key, V chunks of key groups past it hold
-// the last valid group (compute_tile masks both).
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane l
+// writes bytes [16l, 16l + 16) after the wave-uniform LDS address dst.  Completion is counted
+// by the wave's vector memory counter like any load.
+__device__ __forceinline__ void load16_to_lds(const void* src, u32x4_t* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                   kCpolNontemporal);
+}
+
+// s_waitcnt immediate with vmcnt = n (0..63) and the other counters at their maxima
+constexpr int wait_vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Issues this thread's share of the cursor's tile into tile buffer buf, branch-free and clamped
+// like load_tile: K chunks of keys past the valid length hold the last valid key, V chunks of
+// key groups past it hold the last valid group (compute_tile masks both).  Returns whether a
+// page id of the tile was out of range (page 0 is read instead).  Loads per thread: D/64 for
+// K, as many for V with the output.
 template <int D, bool WO>
-__device__ __forceinline__ void load_share(Share<D>& sh, const Cursor& c, Pages pg,
-                                           const Params& p, int tid) {
+__device__ __forceinline__ bool issue_share(const Cursor& c, Pages pg, const Params& p, int tid,
+                                            u32x4_t* buf) {
   constexpr int NC = D / 64;
   const int ntp = c.ntp();
   const bool paged = c.tt < ntp;
@@ -303,35 +322,25 @@ __device__ __forceinline__ void load_share(Share<D>& sh, const Cursor& c, Pages 
   }
   const int p0 = key0 >> log2S;
   const bool two = paged && S < 32;
-  sh.bad = bad;
+  u32x4_t* dst = buf + uni(tid & ~63);  // this wave's 64 chunks
 #pragma unroll
   for (int u = 0; u < NC; ++u) {
     const int i = tid + 256 * u;
     const int key = min(key0 + (i & 31), last);
     const uint16_t* kb = (two && (key >> log2S) != p0) ? k1p : k0p;
-    const uint16_t* ka = kb + ((uint32_t)(((i >> 5) << log2S) + (key & (S - 1))) << 3);
-    sh.k[u] = load16_stream(ka);
+    load16_to_lds(kb + ((uint32_t)(((i >> 5) << log2S) + (key & (S - 1))) << 3), dst + 256 * u);
   }
-  if constexpr (!WO) return;
-#pragma unroll
-  for (int u = 0; u < NC; ++u) {
-    const int j = tid + 256 * u;
-    const int grp = min(key0 + 8 * (j / D), last & ~7);
-    const uint16_t* vb = (two && (grp >> log2S) != p0) ? v1p : v0p;
-    const uint16_t* va = vb + ((uint32_t)(((grp & (S - 1)) >> 3) * D + (j & (D - 1))) << 3);
-    sh.v[u] = load16_stream(va);
-  }
-}
-
-template <int D, bool WO>
-__device__ __forceinline__ void store_share(const Share<D>& sh, u32x4_t* buf, int tid) {
-  constexpr int NC = D / 64;
-#pragma unroll
-  for (int u = 0; u < NC; ++u) buf[tid + 256 * u] = sh.k[u];
   if constexpr (WO) {
 #pragma unroll
-    for (int u = 0; u < NC; ++u) buf[4 * D + tid + 256 * u] = sh.v[u];
+    for (int u = 0; u < NC; ++u) {
+      const int j = tid + 256 * u;
+      const int grp = min(key0 + 8 * (j / D), last & ~7);
+      const uint16_t* vb = (two && (grp >> log2S) != p0) ? v1p : v0p;
+      load16_to_lds(vb + ((uint32_t)(((grp & (S - 1)) >> 3) * D + (j & (D - 1))) << 3),
+                    dst + 4 * D + 256 * u);
+    }
   }
+  return bad;
 }
 
 // The wave's MFMA fragments of a tile from its LDS buffer, the registers load_tile fills: the
@@ -604,7 +613,8 @@ __device__ __forceinline__ int slice_begin(int i, int total, int n) {
 // SH: shared tiles (the workgroup's four waves are four query groups of one kv head; NB is then
 // the number of tiles whose shares are in flight in registers).
 template <int D, int QT, int NB, bool WO, bool SH>
-__global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void attn_kernel(
+__global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
+                                     : ((NB == 2 && QT == 1) ? 2 : 1)) void attn_kernel(
     Params p, const int32_t* __restrict__ page_table) {
   constexpr int NK = D / 32, ND = D / 16, R = 16 * QT;
   extern __shared__ __align__(16) int smem_i[];
@@ -998,46 +1008,51 @@ __global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void att
   };
   bool bad = false;
   if constexpr (SH) {
-    // ---- shared tiles: shares of tiles tv+1 .. tv+NB are in flight in registers while tile tv
-    // is computed from LDS buffer tv % 3.  At step tv the share of tile tv+1 is written to
-    // buffer (tv+1) % 3 -- last read by the computation of tile tv-2, which every wave had
-    // finished before the previous step's barrier -- and its registers take tile tv+1+NB;
-    // after the barrier every share of tile tv is in LDS.  All four waves take the same steps.
-    constexpr int CH = 8 * D;  // 16-byte chunks per tile buffer (K, then V)
+    // ---- shared tiles: tiles tv+1 .. tv+NB-1 are on their way into LDS while tile tv is
+    // computed from buffer tv % (NB+1).  At step tv every thread waits for its own share of
+    // tile tv (its loads complete in issue order: only the NB-1 later tiles' may be pending),
+    // the barrier then makes every share of tile tv visible, and the share of tile tv+NB is
+    // issued into the buffer of tile tv-1, which every wave finished before this barrier.  All
+    // four waves take the same steps.
+    constexpr int NBUF = NB + 1;
+    constexpr int CH = 8 * D;                     // 16-byte chunks per tile buffer (K, then V)
+    constexpr int NL = (WO ? 2 : 1) * (D / 64);   // loads per thread and tile
     u32x4_t* ring = reinterpret_cast<u32x4_t*>(s_q);
-    Share<D> sh[NB];
+    int badbits = 0;  // bit i: the tile in buffer i read an invalid page id
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       if (k > 0 && tvl + 1 < n) next(L, tvl);
-      load_share<D, WO>(sh[k], L, fetch_pages(L, p, page_table), p, tid);
+      const bool b = issue_share<D, WO>(L, fetch_pages(L, p, page_table), p, tid,
+                                        ring + (size_t)k * CH);
+      badbits |= (b ? 1 : 0) << k;
     }
     if (tvl + 1 < n) next(L, tvl);
-    store_share<D, WO>(sh[0], ring, tid);
-    int badbits = sh[0].bad ? 1 : 0;  // bit i: the tile in buffer i read an invalid page id
-    load_share<D, WO>(sh[0], L, fetch_pages(L, p, page_table), p, tid);
-    if (tvl + 1 < n) next(L, tvl);
-    lds_barrier();
     int tv = 0;
-    auto sh_step = [&](Share<D>& Y) {
+    auto sh_step = [&](int rb) {  // rb = tv % NBUF
       const bool live = tv < n;
-      const Pages pg = fetch_pages(L, p, page_table);  // in flight during the LDS writes
-      if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
-      const int wb = (tv + 1) % kShBufs;
-      store_share<D, WO>(Y, ring + (size_t)wb * CH, tid);
-      badbits = (badbits & ~(1 << wb)) | ((Y.bad ? 1 : 0) << wb);
-      load_share<D, WO>(Y, L, pg, p, tid);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      const Pages pg = fetch_pages(L, p, page_table);  // in flight during the wait
+      if (live && tv > 0 && (C.tt == 0 || tv == n1)) {
+        // a new piece's queries: the newest loads, so waiting for them waits for every tile
+        // in flight too (the alternative, a wait at each use, would drain every step)
+        load_q<D, QT>(qf, C, p, lane);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      }
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm((NB - 1) * NL));
       lds_barrier();
+      const int wb = (rb + NB) % NBUF;  // the buffer of tile tv-1
+      const bool b = issue_share<D, WO>(L, pg, p, tid, ring + (size_t)wb * CH);
+      badbits = (badbits & ~(1 << wb)) | ((b ? 1 : 0) << wb);
       if (live) {
-        const int rb = tv % kShBufs;
         const int nq = (C.nrows - C.qg * R + 15) >> 4;
         if (nq > 0) {
           Tile<D> X;
           const int ntp = C.ntp();
-          const bool pg = C.tt < ntp;
+          const bool pgd = C.tt < ntp;
           read_tile_k<D>(X, ring + (size_t)rb * CH, lane);
-          compute_tile<D, QT, WO, false, true>(X, pg ? C.tt * 32 : (C.tt - ntp) * 32,
-                                               pg ? C.plen() : p.blk, nq, qf, o, mrun, lrun,
+          compute_tile<D, QT, WO, false, true>(X, pgd ? C.tt * 32 : (C.tt - ntp) * 32,
+                                               pgd ? C.plen() : p.blk, nq, qf, o, mrun, lrun,
                                                p.scale_log2, lane, ring + (size_t)rb * CH);
         }
         bad = bad || ((badbits >> rb) & 1);
@@ -1053,9 +1068,11 @@ __global__ __launch_bounds__(256, (SH || (NB == 2 && QT == 1)) ? 2 : 1) void att
     };
     while (true) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) sh_step(sh[(j + 1) % NB]);
+      for (int j = 0; j < NBUF; ++j) sh_step(j);
       if (tv >= n) break;
     }
+    // no load into LDS may be pending when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     return;
   }
   Tile<D> tl[NB];
@@ -1120,14 +1137,25 @@ int device_cus() {
   return cached[dev];
 }
 
+// Tiles in flight per wave (one-wave kernels: tile buffers) or per workgroup (shared tiles).
+constexpr int prefetch_of(int QT, bool SH) {
+  return SH ? (QT == 1 ? kShPrefetch : kShPrefetchQt2) : (QT == 1 ? kPrefetchQt1 : 2);
+}
+
+// LDS of one workgroup: the requests' metadata, then the query operands of 64-row waves or the
+// tile ring of shared tiles.
+size_t attn_lds_bytes(int B, int D, int QT, bool SH) {
+  size_t b = (size_t)(4 * B + 1 + 256) * sizeof(int);
+  if (QT >= 4) b = ((b + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
+  if (SH) b = ((b + 15) & ~(size_t)15) + (size_t)(prefetch_of(QT, SH) + 1) * 8 * D * 16;
+  return b;
+}
+
 template <int D, int QT, bool WO, bool SH = false>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
-  size_t shmem = (size_t)(4 * prm.B + 1 + 256) * sizeof(int);
-  if (QT >= 4) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kWaves * QT * (D / 32) * 64 * 16;
-  if (SH) shmem = ((shmem + 15) & ~(size_t)15) + (size_t)kShBufs * 8 * D * 16;
-  constexpr int NB = SH ? (QT == 1 ? kShPrefetch : kShPrefetchQt2) : (QT == 1 ? kPrefetchQt1 : 2);
-  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH>), dim3(plan.wgs), dim3(256), shmem, s, prm,
-                     prm.page_table);
+  constexpr int NB = prefetch_of(QT, SH);
+  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH>), dim3(plan.wgs), dim3(256),
+                     attn_lds_bytes(prm.B, D, QT, SH), s, prm, prm.page_table);
   return hipGetLastError();
 }
 
@@ -1149,13 +1177,18 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
     pl.shared = false;
     pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
     pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
-    pl.wgs = cus * ((pl.qt > 1 && lse_only) ? 2 : kWgsPerCuQt1);
+    pl.wgs = (pl.qt > 1 && lse_only) ? 2 : kWgsPerCuQt1;
   } else {
-    // the four waves of a workgroup on one (request, kv head)'s tiles, two workgroups per CU
+    // the four waves of a workgroup on one (request, kv head)'s tiles
     pl.shared = true;
     pl.qt = rows <= 64 ? 1 : 2;
     pl.nqg = kWaves;
-    pl.wgs = cus * kShWgsPerCu;
+    pl.wgs = pl.qt == 1 ? kShWgsPerCuQt1 : kShWgsPerCu;
+  }
+  // workgroups per CU, as many as the LDS holds at once (large batches: larger metadata)
+  {
+    const int fit = (int)(kLdsPerCu / attn_lds_bytes(B, d, pl.qt, pl.shared));
+    pl.wgs = cus * std::max(1, std::min(pl.wgs, fit));
   }
   const long long ntiles_max = ((long long)max_pages * S + 31) / 32 + (blk + 31) / 32;
   pl.tiles_bound = (long long)B * ntiles_max;
@@ -1176,7 +1209,7 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
   const size_t R = 16 * (size_t)pl.qt;
   // arrival counters sized for the largest grid of either mode, so that the counters of one
   // workspace never overlap another mode's partials
-  pl.cnt_bytes = ((size_t)2 * cus * kWaves * sizeof(int) + 255) & ~(size_t)255;
+  pl.cnt_bytes = ((size_t)kMaxWgsPerCu * cus * kWaves * sizeof(int) + 255) & ~(size_t)255;
   pl.ws_o_bytes = lse_only ? 0 : 2 * W * R * (size_t)d * sizeof(float);
   pl.ws_ml_bytes = 2 * W * 2 * R * sizeof(float);
   pl.ws_bytes = pl.cnt_bytes + pl.ws_o_bytes + pl.ws_ml_bytes;
