@@ -321,6 +321,13 @@ ATTN_CASES = {
     "g4_d64_b2500_shared": ("tiny_b2_blk16", {"B": 2500, "blk": 32, "Hq": 8, "Hkv": 2, "S": 32,
                                               "prefix": ("uniform", 1, 100),
                                               "max_prefix": 128}, 12),
+    # shared tiles at head dim 128 with empty prefixes (block tiles only: one tile per item, a
+    # new piece at every step) and a request without kept tokens among the others (the 19th
+    # for this case's seed)
+    "g4_d128_q64rows_prefix0_shared": ("tiny_b2_blk16", {"B": 24, "blk": 32, "Hq": 8, "Hkv": 2,
+                                                         "d": 128, "S": 64,
+                                                         "prefix": ("uniform", 0, 0),
+                                                         "max_prefix": 64}, 16),
     # 4096 requests' metadata and the tile ring at head dim 128: the LDS holds one shared-tile
     # workgroup per CU, so the grid has one per CU
     "g4_d128_b4096_shared": ("tiny_b2_blk16", {"B": 4096, "blk": 32, "Hq": 8, "Hkv": 2, "d": 128,
