@@ -35,11 +35,12 @@
 //   * V pages [page, Hkv, S/8, d, 8]: a lane's two 8-byte loads are one dim of the two 4-key
 //     runs its S^T lane group holds, which is exactly the A operand of O^T = V^T P^T for that
 //     lane group; P^T (bf16) comes straight from the S^T registers.
-// Shared tiles.  Items of 33..64 rows, and of 65..128 rows with the output, take all four waves
-// of a workgroup, one 16- or 32-row query group each, on the same kv head: the workgroup loads
-// each tile once (every thread loads a 1/256 share straight into a ring of four LDS tile buffers,
-// three tiles ahead, one barrier per tile), and each wave reads the MFMA fragments above from
-// LDS -- the keys, then, after its scores, the values into the same registers.
+// Shared tiles.  Items of 33..64 rows, and of more with the output, take all four waves of a
+// workgroup, one 16- or 32-row query group each, on the same kv head (one workgroup per 128
+// rows): the workgroup loads each tile once (every thread loads a 1/256 share straight into a
+// ring of four LDS tile buffers, three tiles ahead, one barrier per tile), and each wave reads
+// the MFMA fragments above from LDS -- the keys, then, after its scores, the values into the
+// same registers.
 // Softmax is online in the exp2 domain (f32).  Merges run in a fixed order, so results are
 // bitwise reproducible.
 #include <algorithm>
@@ -1167,22 +1168,26 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
   const int G = Hq / Hkv;
   const int rows = max_kept * G;
   const int cus = device_cus();
-  // shared tiles: 33..64 rows (16 per wave), and 65..128 rows with the output (32 per wave)
-  const bool shared = rows > 32 && (rows <= 64 || (rows <= 128 && !lse_only));
+  // shared tiles: 33..64 rows (16 per wave), and with the output any count above 64 (32 per
+  // wave, one workgroup per 128 rows: two or more workgroups of an item stream the same tiles,
+  // the later reads mostly from the XCD's L2)
+  const bool shared = rows > 32 && (rows <= 64 || !lse_only);
   if (!shared) {
     // one wave per item: 16, 32 or 64 rows (several query groups per (request, kv head) past
-    // 64 rows).  One 4-wave workgroup per CU (one wave per SIMD, each with NB tiles of 32 keys
-    // in flight); without the output the larger query tiles are light enough for two
-    // workgroups per CU, which hides their instruction latencies behind each other.
+    // 64 rows, without the output).  One 4-wave workgroup per CU (one wave per SIMD, each with
+    // NB tiles of 32 keys in flight); without the output the larger query tiles are light
+    // enough for two workgroups per CU, which hides their instruction latencies behind each
+    // other.
     pl.shared = false;
     pl.qt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
     pl.nqg = (rows + 16 * pl.qt - 1) / (16 * pl.qt);
     pl.wgs = (pl.qt > 1 && lse_only) ? 2 : kWgsPerCuQt1;
   } else {
-    // the four waves of a workgroup on one (request, kv head)'s tiles
+    // the four waves of a workgroup on one (request, kv head)'s tiles; past 128 rows several
+    // workgroups per item
     pl.shared = true;
     pl.qt = rows <= 64 ? 1 : 2;
-    pl.nqg = kWaves;
+    pl.nqg = kWaves * ((rows + kWaves * 16 * pl.qt - 1) / (kWaves * 16 * pl.qt));
     pl.wgs = pl.qt == 1 ? kShWgsPerCuQt1 : kShWgsPerCu;
   }
   // workgroups per CU, as many as the LDS holds at once (large batches: larger metadata)

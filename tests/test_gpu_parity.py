@@ -328,6 +328,11 @@ ATTN_CASES = {
                                                          "d": 128, "S": 64,
                                                          "prefix": ("uniform", 0, 0),
                                                          "max_prefix": 64}, 16),
+    # 384 rows per item (G = 8, 48 kept): three shared-tile workgroups per item, whose column
+    # groups (six workgroups) do not divide the grid's XCD rounds evenly
+    "g8_q384rows_shared": ("sweep_b128_blk64", {"B": 3, "Hq": 16, "Hkv": 2,
+                                                "prefix": ("uniform", 1, 900),
+                                                "max_prefix": 1024}, 48),
     # 4096 requests' metadata and the tile ring at head dim 128: the LDS holds one shared-tile
     # workgroup per CU, so the grid has one per CU
     "g4_d128_b4096_shared": ("tiny_b2_blk16", {"B": 4096, "blk": 32, "Hq": 8, "Hkv": 2, "d": 128,
