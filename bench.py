@@ -556,9 +556,26 @@ def kv_pass(fs, inp, st, args, stream, flush):
     cm_bytes = 2 * 2 * st.B * st.blk * st.Hkv * st.d * 2 + 16 * st.B
     log(f"[bench] kv write-back {wb_ms * 1000:.1f} us ({wb_bytes / (wb_ms * 1e-3) / 1e9:.0f} GB/s)"
         f"; block commit {cm_ms * 1000:.1f} us ({cm_bytes / (cm_ms * 1e-3) / 1e9:.0f} GB/s)")
+    # conversion of the whole prefix cache from plain head-major rows [pages, Hkv, S, d]
+    pages, Hkv, D8 = inp.k_cache.shape[0], inp.k_cache.shape[1], inp.k_cache.shape[2]
+    k_plain = inp.k_cache.permute(0, 1, 3, 2, 4).reshape(pages, Hkv, S, 8 * D8).contiguous()
+    v_plain = inp.v_cache.permute(0, 1, 2, 4, 3).reshape(pages, Hkv, S, 8 * D8).contiguous()
+    k_out, v_out = torch.empty_like(inp.k_cache), torch.empty_like(inp.v_cache)
+    pk = lambda: F.kv_pack(k_plain, v_plain, k_out=k_out, v_out=v_out)
+    pk()
+    torch.cuda.synchronize()
+    assert torch.equal(k_out.view(torch.int16), inp.k_cache.view(torch.int16))
+    assert torch.equal(v_out.view(torch.int16), inp.v_cache.view(torch.int16))
+    pk_ms = timed(pk, args.steps, flush, stream)
+    pk_bytes = 4 * inp.k_cache.numel() * 2
+    log(f"[bench] kv pack of the prefix cache {pk_bytes / 1e6:.0f} MB moved in {pk_ms * 1000:.1f} "
+        f"us ({pk_bytes / (pk_ms * 1e-3) / 1e9:.0f} GB/s)")
+    del k_plain, v_plain, k_out, v_out
     return {"writeback_us": round(wb_ms * 1000, 2), "writeback_bytes": wb_bytes,
             "commit_us": round(cm_ms * 1000, 2), "commit_bytes": cm_bytes,
-            "commit_hbm_frac": round(cm_bytes / (cm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "commit_hbm_frac": round(cm_bytes / (cm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "pack_us": round(pk_ms * 1000, 2), "pack_bytes": pk_bytes,
+            "pack_hbm_frac": round(pk_bytes / (pk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def main():

@@ -24,6 +24,8 @@ FOCUS_ERR_WORKSPACE = -3
 FOCUS_ERR_HIP = -4
 FOCUS_F32 = 0
 FOCUS_BF16 = 1
+FOCUS_KV_HEAD_MAJOR = 0
+FOCUS_KV_TOKEN_MAJOR = 1
 
 _c_void_p, _c_int, _c_float, _c_size_t = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _c_int64 = ctypes.c_int64
@@ -69,6 +71,7 @@ SIGNATURES = {
     "focus_block_commit": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 2 +
                            [_c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int,
                             _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "focus_kv_pack": (_c_int, [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p] * 3),
 }
 
 
@@ -247,6 +250,32 @@ def kv_writeback(k_rows, v_rows, offsets, kept_pos, k_blk, v_blk):
                                   cap, B, blk, Hkv, d, _ptr(k_blk), _ptr(v_blk),
                                   _stream(k_rows.device))
     _check("focus_kv_writeback", rc)
+
+
+def kv_pack(k_src=None, v_src=None, token_major: bool = False, k_out=None, v_out=None):
+    """K/V stored as plain token rows -> the library's layouts (see focus_kv_pack).
+
+    k_src, v_src: bf16 [n, Hkv, S, d] (token_major=False) or [n, S, Hkv, d] (token_major=True);
+    either may be None.  Returns (k_out [n, Hkv, d/8, S, 8], v_out [n, Hkv, S/8, d, 8]), the
+    missing one as None; outputs are allocated unless given."""
+    src = k_src if k_src is not None else v_src
+    if src is None:
+        raise ValueError("kv_pack needs k_src or v_src")
+    n = src.shape[0]
+    S, Hkv = (src.shape[1], src.shape[2]) if token_major else (src.shape[2], src.shape[1])
+    d = src.shape[3]
+    dev = src.device
+    if k_src is not None and k_out is None:
+        k_out = torch.empty((n, Hkv, d // 8, S, 8), dtype=torch.bfloat16, device=dev)
+    if v_src is not None and v_out is None:
+        v_out = torch.empty((n, Hkv, S // 8, d, 8), dtype=torch.bfloat16, device=dev)
+    layout = FOCUS_KV_TOKEN_MAJOR if token_major else FOCUS_KV_HEAD_MAJOR
+    rc = lib().focus_kv_pack(_ptr(k_src) if k_src is not None else None,
+                             _ptr(v_src) if v_src is not None else None, layout, n, Hkv, S, d,
+                             _ptr(k_out) if k_src is not None else None,
+                             _ptr(v_out) if v_src is not None else None, _stream(dev))
+    _check("focus_kv_pack", rc)
+    return (k_out if k_src is not None else None), (v_out if v_src is not None else None)
 
 
 def block_commit(commit, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len_in,

@@ -494,4 +494,39 @@ int focus_block_commit(const uint8_t* commit, const void* k_blk, const void* v_b
   return status_of(focus::launch_commit(a, stream));
 }
 
+int focus_kv_pack(const void* k_src, const void* v_src, int layout, int n_blocks, int Hkv, int S,
+                  int d, void* k_out, void* v_out, hipStream_t stream) {
+  if ((k_src == nullptr) != (k_out == nullptr) || (v_src == nullptr) != (v_out == nullptr))
+    return FOCUS_ERR_INVALID_ARG;
+  if (k_src == nullptr && v_src == nullptr) return FOCUS_ERR_INVALID_ARG;
+  if (n_blocks <= 0 || Hkv <= 0 || S <= 0 || d <= 0) return FOCUS_ERR_INVALID_ARG;
+  if (layout != FOCUS_KV_HEAD_MAJOR && layout != FOCUS_KV_TOKEN_MAJOR) return FOCUS_ERR_UNSUPPORTED;
+  if (!pow2_in(S, 16, 64) || (d != 64 && d != 128) || Hkv > 64) return FOCUS_ERR_UNSUPPORTED;
+  if ((int64_t)n_blocks * Hkv > INT32_MAX) return FOCUS_ERR_UNSUPPORTED;
+  const void* ptrs[4] = {k_src, v_src, k_out, v_out};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return FOCUS_ERR_INVALID_ARG;
+  // no output may overlap an input or the other output
+  const uintptr_t bytes = (uintptr_t)n_blocks * Hkv * S * d * sizeof(uint16_t);
+  auto overlap = [&](const void* x, const void* y) {
+    if (x == nullptr || y == nullptr) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return a < b + bytes && b < a + bytes;
+  };
+  if (overlap(k_out, k_src) || overlap(k_out, v_src) || overlap(v_out, k_src) ||
+      overlap(v_out, v_src) || overlap(k_out, v_out))
+    return FOCUS_ERR_INVALID_ARG;
+  focus::PackArgs a{};
+  a.k_src = static_cast<const uint16_t*>(k_src);
+  a.v_src = static_cast<const uint16_t*>(v_src);
+  a.token_major = layout == FOCUS_KV_TOKEN_MAJOR;
+  a.n_blocks = n_blocks;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.d = d;
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  return status_of(focus::launch_kv_pack(a, stream));
+}
+
 }  // extern "C"

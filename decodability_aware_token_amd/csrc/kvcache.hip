@@ -1,7 +1,8 @@
 // Intra-block KV write-back and block commit.  Project page "FOCUS: DLLMs Know How to Tame Their
 // Compute Bound", cards "Runtime Action" (intra-block KV caching) and "Motivation" (finished
 // blocks are exactly KV-cached); AI Engineering Academy article on FOCUS, section "Arquitetura do
-// FOCUS" (KV-cache management).  Both are byte moves between the MFMA-native layouts:
+// FOCUS" (KV-cache management).  Both are byte moves between the MFMA-native layouts (as is the
+// conversion of plain token-row K/V into them, at the end of this file):
 //   K [.., Hkv, d/8, n, 8]: key (token t, dim c) at [c/8][t][c%8] -- 16-byte chunks per token
 //   V [.., Hkv, n/8, d, 8]: value (t, c) at [t/8][c][t%8]       -- 16-byte chunks per 8 tokens
 #include <algorithm>
@@ -286,7 +287,69 @@ __global__ __launch_bounds__(256, 3) void block_commit_kernel(CommitArgs a) {
   }
 }
 
+// Conversion of plain K/V (token rows of d elements) into the layouts above, for callers whose
+// cache is stored row by row.  A thread takes one 8-token x 8-dim tile of one (block, kv head):
+// it loads the tile's 8 row pieces (16 bytes each; neighbouring threads read neighbouring
+// pieces of the same rows) and stores
+//  * K: the same 8 pieces as the chunks (dim group, tokens 8q..8q+7) -- consecutive chunks;
+//  * V: the tile transposed in registers, one chunk of 8 tokens per dim -- consecutive chunks;
+// so each thread writes two whole 128-byte runs.  A workgroup covers 256 tiles: one or more
+// (block, kv head) pairs, S*d/64 tiles each.
+__global__ __launch_bounds__(256) void kv_pack_kernel(PackArgs a) {
+  const int D8 = a.d / 8;
+  const int tiles = (a.S / 8) * D8;       // per (block, kv head): 16 .. 128
+  const int per_wg = 256 / tiles;         // pairs per workgroup
+  const int pair = blockIdx.x * per_wg + threadIdx.x / tiles;
+  const int tile = threadIdx.x % tiles;
+  if (threadIdx.x >= per_wg * tiles || pair >= a.n_blocks * a.Hkv) return;
+  const int n = pair / a.Hkv, g = pair % a.Hkv;
+  const int q = tile / D8, c8 = tile % D8;  // tokens 8q..8q+7, dims 8*c8..8*c8+7
+  // source element (token s, dim 8*c8) of (n, g)
+  auto src_at = [&](int s) -> size_t {
+    return a.token_major ? ((((size_t)n * a.S + s) * a.Hkv + g) * a.d + 8 * c8)
+                         : ((((size_t)n * a.Hkv + g) * a.S + s) * a.d + 8 * c8);
+  };
+  const size_t base = (size_t)pair * a.S * a.d;  // (n, g) block of either output
+  uint4 kr[8], vr[8];
+  if (a.k_src != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kr[i] = load16(a.k_src + src_at(8 * q + i));
+  }
+  if (a.v_src != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vr[i] = load16(a.v_src + src_at(8 * q + i));
+  }
+  if (a.k_src != nullptr) {
+    uint16_t* dst = a.k_out + base + ((size_t)c8 * a.S + 8 * q) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) reinterpret_cast<uint4*>(dst)[i] = kr[i];
+  }
+  if (a.v_src != nullptr) {
+    // element e of row i: 16-bit half (e & 1) of word e / 2
+    auto el = [&](int i, int e) -> uint32_t {
+      const uint32_t w = e < 2 ? vr[i].x : e < 4 ? vr[i].y : e < 6 ? vr[i].z : vr[i].w;
+      return (e & 1) ? (w >> 16) : (w & 0xffffu);
+    };
+    uint16_t* dst = a.v_out + base + ((size_t)q * a.d + 8 * c8) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint4 o = make_uint4(el(0, e) | (el(1, e) << 16), el(2, e) | (el(3, e) << 16),
+                                 el(4, e) | (el(5, e) << 16), el(6, e) | (el(7, e) << 16));
+      reinterpret_cast<uint4*>(dst)[e] = o;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_pack(const PackArgs& a, hipStream_t s) {
+  const int tiles = (a.S / 8) * (a.d / 8);
+  const int per_wg = 256 / tiles;
+  const long long pairs = (long long)a.n_blocks * a.Hkv;
+  const int grid = (int)((pairs + per_wg - 1) / per_wg);
+  hipLaunchKernelGGL(kv_pack_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_writeback(const WritebackArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kv_writeback_kernel, dim3(a.B, kWritebackSplit), dim3(256), 0, s, a);

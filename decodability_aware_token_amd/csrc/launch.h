@@ -141,4 +141,15 @@ struct CommitArgs {
 };
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 
+// Conversion of plain token-row K/V into the MFMA-native layouts above.
+struct PackArgs {
+  const uint16_t* k_src;   // [n, Hkv, S, d] (token_major = 0) or [n, S, Hkv, d]; null: no K
+  const uint16_t* v_src;   // same; null: no V
+  int token_major;
+  int n_blocks, Hkv, S, d;
+  uint16_t* k_out;         // [n, Hkv, d/8, S, 8]
+  uint16_t* v_out;         // [n, Hkv, S/8, d, 8]
+};
+hipError_t launch_kv_pack(const PackArgs& a, hipStream_t s);
+
 }  // namespace focus

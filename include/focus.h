@@ -314,6 +314,32 @@ int focus_block_commit(const uint8_t* commit, const void* k_blk, const void* v_b
                        const int32_t* free_pages, int free_cap, const int32_t* free_count_in,
                        int32_t* free_count_out, int32_t* status, hipStream_t stream);
 
+/* --------------------------------------------------------------------------------------------
+ * 7. KV layout conversion.
+ *
+ * Calls 4-6 read and write K/V in the MFMA-native layouts given under call 4 (the pages fix no
+ * KV layout; they call for a paged prefix cache and an intra-block KV cache: project page,
+ * card "Runtime Action" (intra-block KV caching); AI Engineering Academy article, section
+ * "Arquitetura do FOCUS" (KV-cache management)).  This call converts K/V stored as plain token
+ * rows into them.  For block n (a page of the cache, or a request's block), kv head g, token
+ * s < S and dim c < d, the source element is
+ *   layout FOCUS_KV_HEAD_MAJOR  (0): src[n, g, s, c]   (src [n_blocks, Hkv, S, d])
+ *   layout FOCUS_KV_TOKEN_MAJOR (1): src[n, s, g, c]   (src [n_blocks, S, Hkv, d])
+ * and it is written to
+ *   k_out[n, g, c/8, s, c%8] = k_src(n, g, s, c)       (k_out [n_blocks, Hkv, d/8, S, 8])
+ *   v_out[n, g, s/8, c, s%8] = v_src(n, g, s, c)       (v_out [n_blocks, Hkv, S/8, d, 8])
+ * i.e. k_cache / v_cache of call 4 (n = page, S = page size), or k_blk / v_blk (n = request,
+ * S = blk).  All bf16, moved bit for bit.  A pair (k_src, k_out) or (v_src, v_out) may be
+ * both NULL (that matrix is skipped), not one of the two; at least one pair is given.  No
+ * output may overlap an input or the other output (checked on the host).
+ * Supported: S in {16,32,64}; d in {64,128}; 1 <= Hkv <= 64; n_blocks * Hkv < 2^31; pointers
+ * 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+typedef enum { FOCUS_KV_HEAD_MAJOR = 0, FOCUS_KV_TOKEN_MAJOR = 1 } focus_kv_layout;
+
+int focus_kv_pack(const void* k_src, const void* v_src, int layout, int n_blocks, int Hkv, int S,
+                  int d, void* k_out, void* v_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

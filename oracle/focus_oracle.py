@@ -308,6 +308,40 @@ def ragged_paged_attn(q: np.ndarray, offsets: np.ndarray, k_cache, v_cache, page
 # --------------------------------------------------------------------------------------------
 # f3: intra-block KV write-back and block commit
 # --------------------------------------------------------------------------------------------
+def kv_pack(k=None, v=None, token_major: bool = False):
+    """Plain K/V token rows -> the paged layouts `request_kv` reads (the prefix cache of [PP,
+    "Motivation"] and the intra-block cache of [PP, "Runtime Action"] store K/V; the pages fix
+    no layout, these are the library's).
+
+    k, v: [n, Hkv, S, d] (head-major) or [n, S, Hkv, d] (token_major), either may be None; any
+    dtype (a move).  Returns (K [n, Hkv, d/8, S, 8], V [n, Hkv, S/8, d, 8]), None where the input
+    was None: key (s, c) of (block b, head g) at [b, g, c // 8, s, c % 8], value (s, c) at
+    [b, g, s // 8, c, s % 8].
+    """
+    def rows(x):  # [n, Hkv, S, d]
+        x = np.asarray(x)
+        return x.transpose(0, 2, 1, 3) if token_major else x
+
+    kp = vp = None
+    if k is not None:
+        kx = rows(k)
+        n, H, S, d = kx.shape
+        kp = np.zeros((n, H, d // 8, S, 8), dtype=kx.dtype)
+        for b in range(n):
+            for g in range(H):
+                for s in range(S):
+                    kp[b, g, :, s, :] = kx[b, g, s].reshape(d // 8, 8)
+    if v is not None:
+        vx = rows(v)
+        n, H, S, d = vx.shape
+        vp = np.zeros((n, H, S // 8, d, 8), dtype=vx.dtype)
+        for b in range(n):
+            for g in range(H):
+                for s in range(S):
+                    vp[b, g, s // 8, :, s % 8] = vx[b, g, s]
+    return kp, vp
+
+
 def kv_writeback(k_rows, v_rows, offsets, kept_pos, k_blk, v_blk, cap: Optional[int] = None):
     """The kept tokens' fresh K/V replace the cached block KV at their positions; evicted
     positions keep their cached values ([PP, "Runtime Action"]: intra-block KV caching; [NEWS,

@@ -293,3 +293,25 @@ def test_block_commit_errors():
     assert bc(S=48) == F.FOCUS_ERR_UNSUPPORTED
     assert bc(mp=1 << 20) == F.FOCUS_ERR_UNSUPPORTED # max_pages * S > 2^24
     assert bc(kc=P + 8) == F.FOCUS_ERR_INVALID_ARG
+
+
+def test_kv_pack_errors():
+    nb = 4 * 8 * 64 * 128 * 2  # bytes of one matrix at the default sizes
+    def kp(**kw):
+        a = dict(ks=P, vs=P + nb, lay=0, n=4, Hkv=8, S=64, d=128, ko=P + 2 * nb, vo=P + 3 * nb)
+        a.update(kw)
+        return F.lib().focus_kv_pack(a["ks"], a["vs"], a["lay"], a["n"], a["Hkv"], a["S"],
+                                     a["d"], a["ko"], a["vo"], None)
+    assert kp(ks=None) == F.FOCUS_ERR_INVALID_ARG            # a pair with one pointer
+    assert kp(vo=None) == F.FOCUS_ERR_INVALID_ARG
+    assert kp(ks=None, ko=None, vs=None, vo=None) == F.FOCUS_ERR_INVALID_ARG
+    assert kp(n=0) == F.FOCUS_ERR_INVALID_ARG
+    assert kp(lay=2) == F.FOCUS_ERR_UNSUPPORTED
+    assert kp(S=48) == F.FOCUS_ERR_UNSUPPORTED
+    assert kp(S=128) == F.FOCUS_ERR_UNSUPPORTED
+    assert kp(d=96) == F.FOCUS_ERR_UNSUPPORTED
+    assert kp(Hkv=65) == F.FOCUS_ERR_UNSUPPORTED
+    assert kp(n=1 << 30) == F.FOCUS_ERR_UNSUPPORTED          # n_blocks * Hkv >= 2^31
+    assert kp(ko=P + 2 * nb + 8) == F.FOCUS_ERR_INVALID_ARG  # misaligned
+    assert kp(ko=P + nb // 2) == F.FOCUS_ERR_INVALID_ARG     # output overlaps an input
+    assert kp(vo=P + 2 * nb + 16) == F.FOCUS_ERR_INVALID_ARG # the two outputs overlap

@@ -806,6 +806,49 @@ def test_kv_writeback_repeated_and_invalid_positions():
     assert np.array_equal(_bits(kb), ref_k) and np.array_equal(_bits(vb), ref_v)
 
 
+@pytest.mark.parametrize("n,Hkv,S,d,token_major", [(5, 8, 64, 128, False), (7, 4, 16, 128, True),
+                                                   (3, 1, 32, 64, False), (9, 8, 16, 64, True),
+                                                   (33, 3, 64, 64, True),
+                                                   (520, 8, 64, 128, False)])
+def test_kv_pack(n, Hkv, S, d, token_major):
+    # arbitrary 16-bit patterns (NaN payloads included): the conversion is a move
+    _announce(f"kv pack n={n} Hkv={Hkv} S={S} d={d} token_major={token_major}")
+    rng = np.random.default_rng(n * 131 + S)
+    shape = (n, S, Hkv, d) if token_major else (n, Hkv, S, d)
+    k = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    ref_k, ref_v = O.kv_pack(k, v, token_major=token_major)
+    gk, gv = F.kv_pack(bf16_tensor(k, DEV), bf16_tensor(v, DEV), token_major=token_major)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(gk), ref_k) and np.array_equal(_bits(gv), ref_v)
+    # one matrix alone; the other output is not written
+    sentinel = torch.full(tuple(gv.shape), 7.0, dtype=torch.bfloat16, device=DEV)
+    gk2, none = F.kv_pack(bf16_tensor(k, DEV), None, token_major=token_major)
+    _, gv2 = F.kv_pack(None, bf16_tensor(v, DEV), token_major=token_major, v_out=sentinel)
+    torch.cuda.synchronize()
+    assert none is None and gv2 is sentinel
+    assert np.array_equal(_bits(gk2), ref_k) and np.array_equal(_bits(gv2), ref_v)
+
+
+def test_kv_pack_rebuilds_the_step_caches():
+    # the generator's paged caches, unpacked to plain head-major rows, and its block KV from the
+    # token-major layer-1 keys (and the block values unpacked to token-major rows), come back
+    # bit for bit from focus_kv_pack
+    st = make_step(BY_NAME["longctx_b64_blk32"].scaled(B=3))
+    _announce("kv pack of the step caches (longctx, B=3)")
+    pages, Hkv, D8, S, _ = st.k_cache.shape
+    d = 8 * D8
+    k_rows = st.k_cache.transpose(0, 1, 3, 2, 4).reshape(pages, Hkv, S, d)
+    v_rows = st.v_cache.transpose(0, 1, 2, 4, 3).reshape(pages, Hkv, S, d)
+    B, blk = st.k1.shape[0], st.k1.shape[1]
+    v1 = st.v_blk.transpose(0, 2, 4, 1, 3).reshape(B, blk, Hkv, d)  # [B, blk, Hkv, d]
+    gk, gv = F.kv_pack(bf16_tensor(k_rows, DEV), bf16_tensor(v_rows, DEV))
+    bk, bv = F.kv_pack(bf16_tensor(st.k1, DEV), bf16_tensor(v1, DEV), token_major=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(gk), st.k_cache) and np.array_equal(_bits(gv), st.v_cache)
+    assert np.array_equal(_bits(bk), st.k_blk) and np.array_equal(_bits(bv), st.v_blk)
+
+
 def _commit_case(st, rng, nfree, commit, shuffle=True):
     """Device state for a commit: the step's caches plus nfree free pages (the stack)."""
     pool = st.k_cache.shape[0]

@@ -558,6 +558,48 @@ def _logical_block(k_blk, v_blk, r, g):
                         k_blk, v_blk)
 
 
+def test_kv_pack_reads_back_through_the_layout_reader():
+    # Pages packed from plain head-major rows and read through request_kv (the layout reader the
+    # attention pins check against SDPA) give back the rows in order, prefix then block; the
+    # token-major source is the same data transposed.
+    rng = np.random.default_rng(41)
+    B, Hkv, S, d, blk, npg = 2, 3, 16, 16, 16, 3
+    kc_rows = rng.standard_normal((B * npg, Hkv, S, d))
+    vc_rows = rng.standard_normal((B * npg, Hkv, S, d))
+    kb_rows = rng.standard_normal((B, Hkv, blk, d))
+    vb_rows = rng.standard_normal((B, Hkv, blk, d))
+    kc, vc = O.kv_pack(kc_rows, vc_rows)
+    kb, vb = O.kv_pack(kb_rows, vb_rows)
+    table = np.arange(B * npg, dtype=np.int32).reshape(B, npg)[:, ::-1].copy()  # reversed order
+    plen = np.array([npg * S, npg * S - 5], dtype=np.int32)
+    for r in range(B):
+        for g in range(Hkv):
+            K, V = O.request_kv(r, g, kc, vc, table, plen, kb, vb)
+            ek = np.concatenate([kc_rows[table[r], g].reshape(-1, d)[: plen[r]], kb_rows[r, g]])
+            ev = np.concatenate([vc_rows[table[r], g].reshape(-1, d)[: plen[r]], vb_rows[r, g]])
+            np.testing.assert_array_equal(K, ek)
+            np.testing.assert_array_equal(V, ev)
+    tk, tv = O.kv_pack(kc_rows.transpose(0, 2, 1, 3), vc_rows.transpose(0, 2, 1, 3),
+                       token_major=True)
+    np.testing.assert_array_equal(tk, kc)
+    np.testing.assert_array_equal(tv, vc)
+    only_v = O.kv_pack(None, vc_rows)
+    assert only_v[0] is None
+    np.testing.assert_array_equal(only_v[1], vc)
+
+
+def test_kv_pack_matches_the_generator_packers():
+    # The input generator packs its caches with its own reshapes (pack_k / pack_v, token rows
+    # [pages*S, Hkv, d]); the oracle's per-token loops agree with them.
+    rng = np.random.default_rng(43)
+    n, S, Hkv, d = 3, 32, 2, 64
+    tok_k = rng.standard_normal((n * S, Hkv, d))
+    tok_v = rng.standard_normal((n * S, Hkv, d))
+    k, v = O.kv_pack(tok_k.reshape(n, S, Hkv, d), tok_v.reshape(n, S, Hkv, d), token_major=True)
+    np.testing.assert_array_equal(k, pack_k(tok_k, S))
+    np.testing.assert_array_equal(v, pack_v(tok_v, S))
+
+
 def test_kv_writeback_replaces_kept_positions_only():
     rng = np.random.default_rng(31)
     B, blk, Hkv, d = 3, 16, 2, 16
