@@ -288,54 +288,69 @@ __global__ __launch_bounds__(256, 3) void block_commit_kernel(CommitArgs a) {
 }
 
 // Conversion of plain K/V (token rows of d elements) into the layouts above, for callers whose
-// cache is stored row by row.  A thread takes one 8-token x 8-dim tile of one (block, kv head):
-// it loads the tile's 8 row pieces (16 bytes each; neighbouring threads read neighbouring
-// pieces of the same rows) and stores
-//  * K: the same 8 pieces as the chunks (dim group, tokens 8q..8q+7) -- consecutive chunks;
-//  * V: the tile transposed in registers, one chunk of 8 tokens per dim -- consecutive chunks;
-// so each thread writes two whole 128-byte runs.  A workgroup covers 256 tiles: one or more
-// (block, kv head) pairs, S*d/64 tiles each.
+// cache is stored row by row.  A workgroup takes kPackChunks 16-byte chunks of each matrix:
+// one or more consecutive (block, kv head) pairs, whose outputs are one contiguous range.  The
+// source rows are loaded (neighbouring threads read neighbouring chunks of a row) into LDS as
+// they are (rows padded by one chunk, so that reading down a column is free of bank
+// conflicts), then every thread builds output chunks in output order -- a key chunk is one
+// 16-byte piece of a row, a value chunk gathers one dim of 8 consecutive rows -- so that the
+// stores of a wave cover whole consecutive runs.
+constexpr int kPackChunks = 1024;
+
 __global__ __launch_bounds__(256) void kv_pack_kernel(PackArgs a) {
-  const int D8 = a.d / 8;
-  const int tiles = (a.S / 8) * D8;       // per (block, kv head): 16 .. 128
-  const int per_wg = 256 / tiles;         // pairs per workgroup
-  const int pair = blockIdx.x * per_wg + threadIdx.x / tiles;
-  const int tile = threadIdx.x % tiles;
-  if (threadIdx.x >= per_wg * tiles || pair >= a.n_blocks * a.Hkv) return;
-  const int n = pair / a.Hkv, g = pair % a.Hkv;
-  const int q = tile / D8, c8 = tile % D8;  // tokens 8q..8q+7, dims 8*c8..8*c8+7
-  // source element (token s, dim 8*c8) of (n, g)
-  auto src_at = [&](int s) -> size_t {
-    return a.token_major ? ((((size_t)n * a.S + s) * a.Hkv + g) * a.d + 8 * c8)
-                         : ((((size_t)n * a.Hkv + g) * a.S + s) * a.d + 8 * c8);
-  };
-  const size_t base = (size_t)pair * a.S * a.d;  // (n, g) block of either output
-  uint4 kr[8], vr[8];
-  if (a.k_src != nullptr) {
+  constexpr int kMaxRows = kPackChunks / 8;  // d = 64: 8 chunks per row
+  __shared__ uint4 s_k[kPackChunks + kMaxRows], s_v[kPackChunks + kMaxRows];
+  const int tid = threadIdx.x;
+  const int D8 = a.d / 8, pitch = D8 + 1;     // row pitch in chunks
+  const int S = a.S, per_pair = S * D8;        // chunks of one (block, kv head) pair
+  const int pp = kPackChunks / per_pair;       // pairs per workgroup (1 .. 8)
+  const long long pairs = (long long)a.n_blocks * a.Hkv;
+  const long long pair0 = (long long)blockIdx.x * pp;
+  const bool has_k = a.k_src != nullptr, has_v = a.v_src != nullptr;
+  constexpr int U = kPackChunks / 256;
+  uint4 kv[U], vv[U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = load16(a.k_src + src_at(8 * q + i));
+  for (int u = 0; u < U; ++u) {
+    const int i = tid + 256 * u, row = i / D8, c8 = i % D8;
+    const int p = row / S, s = row % S;
+    const long long pair = min(pair0 + p, pairs - 1);  // the last workgroup's unused rows
+    const long long n = pair / a.Hkv, g = pair % a.Hkv;
+    const size_t off = a.token_major ? (((size_t)n * S + s) * a.Hkv + g) * a.d + 8 * c8
+                                     : (((size_t)n * a.Hkv + g) * S + s) * a.d + 8 * c8;
+    if (has_k) kv[u] = load16(a.k_src + off);
+    if (has_v) vv[u] = load16(a.v_src + off);
   }
-  if (a.v_src != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vr[i] = load16(a.v_src + src_at(8 * q + i));
+  for (int u = 0; u < U; ++u) {
+    const int i = tid + 256 * u, row = i / D8, c8 = i % D8;
+    if (has_k) s_k[row * pitch + c8] = kv[u];
+    if (has_v) s_v[row * pitch + c8] = vv[u];
   }
-  if (a.k_src != nullptr) {
-    uint16_t* dst = a.k_out + base + ((size_t)c8 * a.S + 8 * q) * 8;
+  __syncthreads();
+  const size_t out0 = (size_t)pair0 * S * a.d;  // first element of this workgroup's outputs
+  const long long live = min((long long)pp, pairs - pair0) * per_pair;  // chunks to write
+  if (has_k) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) reinterpret_cast<uint4*>(dst)[i] = kr[i];
+    for (int u = 0; u < U; ++u) {
+      const int j = tid + 256 * u;  // output chunk: pair p, dim group c8, token s
+      if (j >= live) break;
+      const int p = j / per_pair, rem = j % per_pair, c8 = rem / S, s = rem % S;
+      reinterpret_cast<uint4*>(a.k_out + out0)[j] = s_k[(p * S + s) * pitch + c8];
+    }
   }
-  if (a.v_src != nullptr) {
-    // element e of row i: 16-bit half (e & 1) of word e / 2
-    auto el = [&](int i, int e) -> uint32_t {
-      const uint32_t w = e < 2 ? vr[i].x : e < 4 ? vr[i].y : e < 6 ? vr[i].z : vr[i].w;
-      return (e & 1) ? (w >> 16) : (w & 0xffffu);
-    };
-    uint16_t* dst = a.v_out + base + ((size_t)q * a.d + 8 * c8) * 8;
+  if (has_v) {
+    const uint16_t* sv = reinterpret_cast<const uint16_t*>(s_v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint4 o = make_uint4(el(0, e) | (el(1, e) << 16), el(2, e) | (el(3, e) << 16),
-                                 el(4, e) | (el(5, e) << 16), el(6, e) | (el(7, e) << 16));
-      reinterpret_cast<uint4*>(dst)[e] = o;
+    for (int u = 0; u < U; ++u) {
+      const int j = tid + 256 * u;  // output chunk: pair p, token group q, dim c
+      if (j >= live) break;
+      const int p = j / per_pair, rem = j % per_pair, q = rem / a.d, c = rem % a.d;
+      const uint16_t* col = sv + (size_t)(p * S + 8 * q) * pitch * 8 + c;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)col[(2 * k) * pitch * 8] | ((uint32_t)col[(2 * k + 1) * pitch * 8] << 16);
+      reinterpret_cast<uint4*>(a.v_out + out0)[j] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -343,10 +358,9 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(PackArgs a) {
 }  // namespace
 
 hipError_t launch_kv_pack(const PackArgs& a, hipStream_t s) {
-  const int tiles = (a.S / 8) * (a.d / 8);
-  const int per_wg = 256 / tiles;
+  const int pp = kPackChunks / (a.S * (a.d / 8));
   const long long pairs = (long long)a.n_blocks * a.Hkv;
-  const int grid = (int)((pairs + per_wg - 1) / per_wg);
+  const int grid = (int)((pairs + pp - 1) / pp);
   hipLaunchKernelGGL(kv_pack_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
