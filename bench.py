@@ -1,8 +1,9 @@
 """Throughput of the focused block-diffusion step on one MI355X.
 
 A step is one pass of the whole hot path over one batch: importance scoring (layer 1 minus
-layer 0), budgeted top-k selection, compaction + gather of the hidden states and of the
-attention queries, and ragged paged attention over each request's paged prefix plus block KV.
+layer 0), budgeted top-k selection, compaction + gather of the hidden states, and ragged paged
+attention of the kept tokens (their queries read in place at the kept positions) over each
+request's paged prefix plus block KV.
 Inputs are seeded synthetic tensors already resident in HBM.  One JSON line is printed.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-graph]
@@ -418,10 +419,10 @@ class Flush:
 
 def front_end_batch(args):
     """The front end alone at batch args.front_end_batch with the workload's shapes: layer-0/1
-    Q/K, hidden states and attention queries drawn on the device from a seeded generator, each
-    position masked with probability 0.8, the budget ceil(0.125 * masked count) (the headline's
-    rule).  Prints one JSON line: mean us per call (caches flushed before each) and the score
-    inputs' bytes."""
+    Q/K and hidden states drawn on the device from a seeded generator, each position masked
+    with probability 0.8, the budget ceil(0.125 * masked count) (the headline's rule); the
+    hidden states are gathered (the attention reads its queries in place).  Prints one JSON
+    line: mean us per call (caches flushed before each) and the score inputs' bytes."""
     import torch
     from decodability_aware_token_amd import binding as F
     from workloads import BY_NAME
@@ -436,7 +437,7 @@ def front_end_batch(args):
     k0, k1 = draw(B, blk, Hkv, d), draw(B, blk, Hkv, d)
     masked = (torch.rand(B, blk, device=dev, generator=g) < 0.8).to(torch.uint8)
     budget = torch.ceil(0.125 * masked.sum(1).float()).to(torch.int32)
-    sets = [draw(B, blk, W), draw(B, blk, Hq, d)]
+    sets = [draw(B, blk, W)]
     cap = B * blk
     outs = dict(delta=torch.empty(B, blk, device=dev),
                 keep=torch.empty(B, blk, dtype=torch.uint8, device=dev),
@@ -517,14 +518,14 @@ def full_domain_pass(inp, t, st, args, stream, flush):
 
 
 def kv_pass(fs, inp, st, args, stream, flush):
-    """Intra-block KV write-back of the kept rows (fresh K/V stand-ins: the gathered Q rows'
-    first Hkv heads) and the commit of every request's block into its paged prefix, each timed
-    by HIP events; the commit runs on a copy of the caches extended by free pages."""
+    """Intra-block KV write-back of the kept rows (fresh K/V stand-ins: the first Hkv heads of
+    the block's query rows) and the commit of every request's block into its paged prefix, each
+    timed by HIP events; the commit runs on a copy of the caches extended by free pages."""
     import torch
     from decodability_aware_token_amd import binding as F
     dev = inp.q_att.device
     T = int(fs.offsets[-1])
-    rows = fs.q_rows[:, : st.Hkv].contiguous()        # [cap, Hkv, d] bf16
+    rows = inp.q_att.reshape(-1, st.Hq, st.d)[: fs.cap, : st.Hkv].contiguous()  # [cap, Hkv, d]
     kb, vb = inp.k_blk.clone(), inp.v_blk.clone()
     S = st.S
     extra = st.B * (-(-st.blk // S) + 1)

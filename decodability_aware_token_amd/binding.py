@@ -50,6 +50,11 @@ SIGNATURES = {
                                          _c_void_p] + [_c_int] * 7 + [_c_float, _c_void_p,
                                                                       _c_void_p, _c_void_p,
                                                                       _c_size_t, _c_void_p]),
+    "focus_ragged_paged_attn_pos": (_c_int, [_c_void_p] * 3 + [_c_int, _c_void_p, _c_void_p,
+                                             _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                             _c_void_p] + [_c_int] * 7 + [_c_float, _c_void_p,
+                                                                          _c_void_p, _c_void_p,
+                                                                          _c_size_t, _c_void_p]),
     "focus_score_select": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_void_p,
                                                                   _c_void_p, _c_int, _c_float,
                                                                   _c_int, _c_int, _c_void_p,
@@ -238,6 +243,32 @@ def ragged_paged_attn(q, offsets, k_cache, v_cache, page_table, prefix_len, k_bl
                                        int(max_kept), float(sm_scale), _ptr(out), _ptr(lse),
                                        _ptr(workspace), wsb, _stream(dev))
     _check("focus_ragged_paged_attn", rc)
+    return out, lse
+
+
+def ragged_paged_attn_pos(q_block, kept_pos, offsets, k_cache, v_cache, page_table, prefix_len,
+                          k_blk, v_blk, max_kept: int, sm_scale: float, out=None, lse=None,
+                          want_lse=True, workspace=None):
+    """ragged_paged_attn with the queries read in place (see focus_ragged_paged_attn_pos):
+    q_block [B, blk, Hq, d] bf16 and kept_pos [cap] i32; out [cap, Hq, d], lse [cap, Hq]."""
+    B, blk, Hq, d = q_block.shape
+    cap = kept_pos.shape[0]
+    num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
+    S = k_cache.shape[3]
+    max_pages = page_table.shape[1]
+    dev = q_block.device
+    if out is None:
+        out = torch.empty((cap, Hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((cap, Hq), dtype=torch.float32, device=dev)
+    need = attn_workspace_bytes(B, blk, Hq, Hkv, d, S, max_pages, max_kept)
+    workspace, wsb = _workspace(need, dev, workspace)
+    rc = lib().focus_ragged_paged_attn_pos(
+        _ptr(q_block), _ptr(kept_pos), _ptr(offsets), cap, _ptr(k_cache), _ptr(v_cache),
+        num_pages, _ptr(page_table), max_pages, _ptr(prefix_len), _ptr(k_blk), _ptr(v_blk), B, blk,
+        Hq, Hkv, d, S, int(max_kept), float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
+        _stream(dev))
+    _check("focus_ragged_paged_attn_pos", rc)
     return out, lse
 
 

@@ -367,16 +367,21 @@ size_t focus_ragged_paged_attn_workspace_size(int B, int blk, int Hq, int Hkv, i
                   focus::plan_attn(B, blk, Hq, Hkv, d, S, max_pages, max_kept, true).ws_bytes);
 }
 
-int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, const void* k_cache,
-                            const void* v_cache, int num_pages, const int32_t* page_table,
-                            int max_pages, const int32_t* prefix_len, const void* k_blk,
-                            const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
-                            int max_kept, float sm_scale, void* out, float* lse, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The attention's checks and launch; q_pos == nullptr: q holds the compacted rows [cap, Hq, d],
+// else the block's queries [B, blk, Hq, d], read at q_pos (call 4b).
+int attn_call(const void* q, const int32_t* q_pos, const int32_t* offsets, int cap,
+              const void* k_cache, const void* v_cache, int num_pages,
+              const int32_t* page_table, int max_pages, const int32_t* prefix_len,
+              const void* k_blk, const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
+              int max_kept, float sm_scale, void* out, float* lse, void* workspace,
+              size_t workspace_bytes, bool positional, hipStream_t stream) {
   // out == NULL: log-sum-exp only (lse required; the values are then not read and may be NULL)
   const bool lse_only = out == nullptr;
   if (!offsets || !prefix_len || !k_blk || (!lse_only && !v_blk)) return FOCUS_ERR_INVALID_ARG;
   if (cap > 0 && (!q || (lse_only && !lse))) return FOCUS_ERR_INVALID_ARG;
+  if (positional && cap > 0 && !q_pos) return FOCUS_ERR_INVALID_ARG;
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || S <= 0 || cap < 0 ||
       num_pages < 0 || max_pages < 0 || max_kept <= 0)
     return FOCUS_ERR_INVALID_ARG;
@@ -400,6 +405,7 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
   if (cap == 0) return FOCUS_OK;
   focus::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
+  a.q_pos = positional ? q_pos : nullptr;
   a.offsets = offsets;
   a.cap = cap;
   a.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -422,6 +428,31 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
   a.lse = lse;
   a.workspace = workspace;
   return status_of(focus::launch_attn(a, plan, stream));
+}
+
+}  // namespace
+
+int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, const void* k_cache,
+                            const void* v_cache, int num_pages, const int32_t* page_table,
+                            int max_pages, const int32_t* prefix_len, const void* k_blk,
+                            const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
+                            int max_kept, float sm_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return attn_call(q, nullptr, offsets, cap, k_cache, v_cache, num_pages, page_table, max_pages,
+                   prefix_len, k_blk, v_blk, B, blk, Hq, Hkv, d, S, max_kept, sm_scale, out, lse,
+                   workspace, workspace_bytes, false, stream);
+}
+
+int focus_ragged_paged_attn_pos(const void* q_block, const int32_t* kept_pos,
+                                const int32_t* offsets, int cap, const void* k_cache,
+                                const void* v_cache, int num_pages, const int32_t* page_table,
+                                int max_pages, const int32_t* prefix_len, const void* k_blk,
+                                const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
+                                int max_kept, float sm_scale, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attn_call(q_block, kept_pos, offsets, cap, k_cache, v_cache, num_pages, page_table,
+                   max_pages, prefix_len, k_blk, v_blk, B, blk, Hq, Hkv, d, S, max_kept, sm_scale,
+                   out, lse, workspace, workspace_bytes, true, stream);
 }
 
 

@@ -84,7 +84,8 @@ constexpr int kMaxMerge = 8;
 constexpr int kMinTilesPerWave = 12;
 
 struct Params {
-  const uint16_t* q;
+  const uint16_t* q;       // [cap, Hq, d] compacted rows, or [B, blk, Hq, d] with q_pos
+  const int32_t* q_pos;    // null, or [cap]: row n of request r is q[r, q_pos[n]]
   const int32_t* offsets;
   const uint16_t* k_cache;
   const uint16_t* v_cache;
@@ -395,17 +396,28 @@ struct QOperand {
 
 // Loads the Q operand of the cursor's item.  Rows past the item's rows (or past cap) are
 // clamped to a valid row: their results are never written, and finite inputs keep them finite.
+// With q_pos the rows are read where they are, at the kept positions of the request's block:
+// a position outside the block reads position 0 and is reported (true: the item's rows become
+// NaN).
 template <int D, int QT>
-__device__ __forceinline__ void load_q(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
+__device__ __forceinline__ bool load_q(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
                                        int lane) {
   constexpr int NK = D / 32, R = 16 * QT;
   const int m16 = lane & 15, j4 = lane >> 4;
+  bool bad = false;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int rho = min(c.qg * R + 16 * qt + m16, c.nrows - 1);
     const int tok = min(c.off0 + (rho >> p.log2G), p.cap - 1);
+    int src = tok;
+    if (p.q_pos != nullptr) {  // wave-uniform
+      const int j = p.q_pos[tok];
+      const bool out = (unsigned)j >= (unsigned)p.blk;
+      bad = bad || out;
+      src = c.r * p.blk + (out ? 0 : j);
+    }
     const uint16_t* qrow =
-        p.q + ((size_t)tok * p.Hq + c.g * p.G + (rho & (p.G - 1))) * D + 8 * j4;
+        p.q + ((size_t)src * p.Hq + c.g * p.G + (rho & (p.G - 1))) * D + 8 * j4;
     if constexpr (QOperand<D, QT>::kLds) {
       u32x4_t t[NK];
 #pragma unroll
@@ -417,6 +429,7 @@ __device__ __forceinline__ void load_q(QOperand<D, QT>& qf, const Cursor& c, con
       for (int kk = 0; kk < NK; ++kk) qf.r[qt][kk] = load16v(qrow + 32 * kk);
     }
   }
+  return bad;
 }
 
 // Scores of one query tile from its Q^T fragments: S^T (32 keys x 16 rows) as two 16-key
@@ -997,7 +1010,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
   QOperand<D, QT> qf;
   if constexpr (QOperand<D, QT>::kLds)
     qf.lds = reinterpret_cast<u32x4_t*>(s_q) + (size_t)wave * QT * NK * 64;
-  load_q<D, QT>(qf, C, p, lane);
+  bool qbad = load_q<D, QT>(qf, C, p, lane);  // the current item's rows read a bad position
   Cursor L = C;
   int tvl = 0, tvc = 0;  // processing indices of L and C
   auto next = [&](Cursor& c, int& idx) {
@@ -1035,7 +1048,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
       if (live && tv > 0 && (C.tt == 0 || tv == n1)) {
         // a new piece's queries: the newest loads, so waiting for them waits for every tile
         // in flight too (the alternative, a wait at each use, would drain every step)
-        load_q<D, QT>(qf, C, p, lane);
+        qbad = load_q<D, QT>(qf, C, p, lane);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1058,7 +1071,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
         }
         bad = bad || ((badbits >> rb) & 1);
         if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
-          finalize(C, bad);
+          finalize(C, bad || qbad);
           reset();
           bad = false;
         }
@@ -1091,7 +1104,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
   auto step = [&](Tile<D>& X, Tile<D>& Y) {
     const bool live = tv < n;
     const Pages pg = fetch_pages(L, p, page_table);
-    if (live && tv > 0 && (C.tt == 0 || tv == n1)) load_q<D, QT>(qf, C, p, lane);
+    if (live && tv > 0 && (C.tt == 0 || tv == n1)) qbad = load_q<D, QT>(qf, C, p, lane);
     load_tile<D, WO>(Y, L, pg, p, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     if (live) {
@@ -1102,7 +1115,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
                               qf, o, mrun, lrun, p.scale_log2, lane);
       bad = bad || X.bad;
       if (C.tt == item_tiles(C, p) - 1 || tv == n1 - 1 || tv == n - 1) {
-        finalize(C, bad);
+        finalize(C, bad || qbad);
         reset();
         bad = false;
       }
@@ -1224,6 +1237,7 @@ AttnPlan plan_attn(int B, int blk, int Hq, int Hkv, int d, int S, int max_pages,
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
   Params prm{};
   prm.q = a.q;
+  prm.q_pos = a.q_pos;
   prm.offsets = a.offsets;
   prm.k_cache = a.k_cache;
   prm.v_cache = a.v_cache;

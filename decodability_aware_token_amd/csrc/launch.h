@@ -74,7 +74,8 @@ size_t score_workspace_bytes(int B, int blk, int Hkv);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 
 struct AttnArgs {
-  const uint16_t* q;
+  const uint16_t* q;       // [cap, Hq, d], or [B, blk, Hq, d] read at q_pos
+  const int32_t* q_pos;    // null or [cap] (kept positions)
   const int32_t* offsets;
   int cap;
   const uint16_t* k_cache;

@@ -1,10 +1,13 @@
-"""One focused block-diffusion step on the GPU: score -> select -> compact (hidden, Q) -> attend.
+"""One focused block-diffusion step on the GPU: score -> select -> compact (hidden) -> attend.
 
 `FocusStep` preallocates every output and workspace once for a fixed batch shape, then `run()`
 issues the C-ABI calls back to back on the current stream with no host synchronisation: ragged
 sizes stay on the device, and the attention is sized by the host-known bound max_kept.  With
 per-request budgets the front end (score, select, compact) is one call of two launches; with the
-adaptive rule it is two calls (score + select, then compaction).
+adaptive rule it is two calls (score + select, then compaction).  The attention reads the kept
+tokens' queries in place, at their kept positions (focus_ragged_paged_attn_pos), so the
+compaction gathers only the hidden states; gather_q=True gathers the queries too and runs the
+attention on the compacted copy (focus_ragged_paged_attn), with the same results.
 `capture()` records one step into a HIP graph (no allocation, no memset node: the kernels reset
 their own arrival counters), and `replay()` launches it, for callers that replay a fixed step.
 With the host ahead of the device the eager launches leave no gap between the kernels; on
@@ -44,7 +47,8 @@ class StepInputs:
 
 
 class FocusStep:
-    def __init__(self, inp: StepInputs, cap: Optional[int] = None, want_lse: bool = True):
+    def __init__(self, inp: StepInputs, cap: Optional[int] = None, want_lse: bool = True,
+                 gather_q: bool = False):
         B, blk, Hq, d = inp.q_att.shape
         Hkv = inp.k_blk.shape[1]
         dev = inp.q_att.device
@@ -56,7 +60,9 @@ class FocusStep:
         self.kept_count = torch.empty(B, dtype=torch.int32, device=dev)
         self.offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
         self.kept_pos = torch.empty(max(self.cap, 1), dtype=torch.int32, device=dev)
-        self.q_rows = torch.empty((max(self.cap, 1), Hq, d), dtype=torch.bfloat16, device=dev)
+        self.gather_q = gather_q
+        self.q_rows = torch.empty((max(self.cap, 1), Hq, d), dtype=torch.bfloat16, device=dev) \
+            if gather_q else None
         self.hidden_rows = None
         if inp.hidden is not None:
             self.hidden_rows = torch.empty((max(self.cap, 1), inp.hidden.shape[2]),
@@ -80,9 +86,9 @@ class FocusStep:
                         kept_count=self.kept_count)
 
     def compact_hidden(self):
-        if self.inp.hidden is not None:
-            F.compact(self.keep, self.inp.hidden, self.cap, offsets=self.offsets,
-                      kept_pos=self.kept_pos, gathered=self.hidden_rows)
+        """Offsets, kept positions and (if the step has them) the gathered hidden states."""
+        F.compact(self.keep, self.inp.hidden, self.cap, offsets=self.offsets,
+                  kept_pos=self.kept_pos, gathered=self.hidden_rows)
 
     def compact_q(self):
         F.compact(self.keep, self.inp.q_att, self.cap, offsets=self.offsets,
@@ -90,9 +96,16 @@ class FocusStep:
 
     def attend(self):
         i = self.inp
-        F.ragged_paged_attn(self.q_rows, self.offsets, i.k_cache, i.v_cache, i.page_table,
-                            i.prefix_len, i.k_blk, i.v_blk, i.max_kept, i.sm_scale, out=self.out,
-                            lse=self.lse, want_lse=self.lse is not None, workspace=self.ws_attn)
+        if self.gather_q:
+            F.ragged_paged_attn(self.q_rows, self.offsets, i.k_cache, i.v_cache, i.page_table,
+                                i.prefix_len, i.k_blk, i.v_blk, i.max_kept, i.sm_scale,
+                                out=self.out, lse=self.lse, want_lse=self.lse is not None,
+                                workspace=self.ws_attn)
+        else:
+            F.ragged_paged_attn_pos(i.q_att, self.kept_pos, self.offsets, i.k_cache, i.v_cache,
+                                    i.page_table, i.prefix_len, i.k_blk, i.v_blk, i.max_kept,
+                                    i.sm_scale, out=self.out, lse=self.lse,
+                                    want_lse=self.lse is not None, workspace=self.ws_attn)
 
     def score_select(self):
         i = self.inp
@@ -106,13 +119,18 @@ class FocusStep:
                         gathered=outs)
 
     def _row_sets(self):
-        sets = [self.inp.q_att] if self.inp.hidden is None else [self.inp.hidden, self.inp.q_att]
-        outs = [self.q_rows] if self.inp.hidden is None else [self.hidden_rows, self.q_rows]
+        sets, outs = [], []
+        if self.inp.hidden is not None:
+            sets.append(self.inp.hidden)
+            outs.append(self.hidden_rows)
+        if self.gather_q:
+            sets.append(self.inp.q_att)
+            outs.append(self.q_rows)
         return sets, outs
 
     def score_select_compact(self):
-        """Score partials, then reduction + selection + compaction in one launch (per-request
-        budgets only)."""
+        """Score partials, then reduction + selection + compaction (hidden states, and the
+        queries with gather_q) in one launch (per-request budgets only)."""
         i = self.inp
         sets, outs = self._row_sets()
         F.score_select_compact(i.q0, i.k0, i.q1, i.k1, i.sm_scale, i.masked, i.budget, sets,
@@ -136,11 +154,13 @@ class FocusStep:
         self.attend()
 
     def run_unfused(self):
-        """The same step as five separate calls (one per entry point of the path)."""
+        """The same step as separate calls, one per entry point of the path (the queries'
+        compaction only with gather_q)."""
         self.score()
         self.select()
         self.compact_hidden()
-        self.compact_q()
+        if self.gather_q:
+            self.compact_q()
         self.attend()
 
     def capture(self):

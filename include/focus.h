@@ -264,6 +264,27 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
                             size_t workspace_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------------
+ * 4b. Ragged paged attention with the queries read in place.
+ *
+ * The same operation and results as call 4 (same section of the pages: ragged execution of the
+ * kept tokens only), with the kept tokens' queries read from the block's query tensor at their
+ * positions instead of from a compacted copy, so the compaction need not gather them: row n
+ * (offsets[r] <= n < offsets[r+1]) has the query q_block[r, kept_pos[n], h, :].
+ *   q_block  [B, blk, Hq, d] bf16;  kept_pos [cap] i32 (as produced by focus_compact or the
+ *            fused front ends)
+ *   every other argument, layout, workspace and supported size as in call 4.
+ * Device data the host cannot check: a position outside [0, blk) gives NaN in all rows of its
+ * request's kv-head group (as an invalid page id does) instead of a memory access.
+ * ------------------------------------------------------------------------------------------ */
+int focus_ragged_paged_attn_pos(const void* q_block, const int32_t* kept_pos,
+                                const int32_t* offsets, int cap, const void* k_cache,
+                                const void* v_cache, int num_pages, const int32_t* page_table,
+                                int max_pages, const int32_t* prefix_len, const void* k_blk,
+                                const void* v_blk, int B, int blk, int Hq, int Hkv, int d, int S,
+                                int max_kept, float sm_scale, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------------
  * 5. Intra-block KV write-back.
  *
  * Project page, card "Runtime Action" (intra-block KV caching): the layer's fresh K/V of the kept

@@ -32,8 +32,8 @@ def step_inputs(st, device="cuda") -> StepInputs:
     return StepInputs(**{k: t[k] for k in _FIELDS})
 
 
-def run_gpu_step(st, cap=None, device="cuda"):
-    fs = FocusStep(step_inputs(st, device), cap=cap)
+def run_gpu_step(st, cap=None, device="cuda", gather_q=False):
+    fs = FocusStep(step_inputs(st, device), cap=cap, gather_q=gather_q)
     fs.run()
     torch.cuda.synchronize()
     return fs, fetch(fs)
@@ -54,9 +54,10 @@ def fetch(fs: FocusStep) -> dict:
         "kept_pos": fs.kept_pos[:T].cpu().numpy(),
         "out": fs.out[:T].float().cpu().numpy().astype(np.float64),
         "out_bits": bf16_to_np(fs.out[:T]),
-        "q_rows": bf16_to_np(fs.q_rows[:T]),
         "lse": None if fs.lse is None else fs.lse[:T].cpu().numpy().astype(np.float64),
     }
+    if fs.q_rows is not None:
+        res["q_rows"] = bf16_to_np(fs.q_rows[:T])
     if fs.hidden_rows is not None:
         res["hidden_rows"] = bf16_to_np(fs.hidden_rows[:T])
     return res
@@ -130,9 +131,12 @@ def check_ragged(gpu, ref, B, excused, rule, gathered=None):
 
 
 def gathered_sets(gpu, st, ref_keep):
-    """(gpu rows, oracle rows, source) of the attention queries and, if gathered, the hidden
-    states: the oracle's compaction of the same sources under its own kept sets."""
-    sets = [(gpu["q_rows"], O.compact(ref_keep, st.q_att)[2], st.q_att)]
+    """(gpu rows, oracle rows, source) of the gathered row sets (the hidden states, and the
+    attention queries when the step gathers them): the oracle's compaction of the same sources
+    under its own kept sets."""
+    sets = []
+    if "q_rows" in gpu:
+        sets.append((gpu["q_rows"], O.compact(ref_keep, st.q_att)[2], st.q_att))
     if "hidden_rows" in gpu:
         sets.append((gpu["hidden_rows"], O.compact(ref_keep, st.hidden)[2], st.hidden))
     return sets

@@ -234,6 +234,24 @@ def test_attn_errors():
     assert _attn(cap=0, q=None, out=None, S=48) == F.FOCUS_ERR_UNSUPPORTED
 
 
+def test_attn_pos_errors():
+    def ap(**kw):
+        a = dict(q=P, pos=P, off=P, cap=64, kc=P, vc=P, npages=100, pt=P, maxp=16, pl=P, kb=P,
+                 vb=P, B=4, blk=32, Hq=32, Hkv=8, d=128, S=64, mk=4, sc=0.088, out=P, lse=P,
+                 ws=P, wsb=1 << 40)
+        a.update(kw)
+        return F.lib().focus_ragged_paged_attn_pos(
+            a["q"], a["pos"], a["off"], a["cap"], a["kc"], a["vc"], a["npages"], a["pt"],
+            a["maxp"], a["pl"], a["kb"], a["vb"], a["B"], a["blk"], a["Hq"], a["Hkv"], a["d"],
+            a["S"], a["mk"], a["sc"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+    assert ap(pos=None) == F.FOCUS_ERR_INVALID_ARG              # the kept positions are needed
+    assert ap(q=None) == F.FOCUS_ERR_INVALID_ARG
+    assert ap(q=P + 8) == F.FOCUS_ERR_INVALID_ARG               # misaligned
+    assert ap(S=48) == F.FOCUS_ERR_UNSUPPORTED                  # as call 4
+    assert ap(ws=None, maxp=128) == F.FOCUS_ERR_WORKSPACE
+    assert ap(cap=0, q=None, pos=None, out=None) == F.FOCUS_OK  # nothing kept: nothing launched
+
+
 def test_attn_plan_is_bounded():
     # the workspace grows with batch, heads and maximal prefix, never with the data
     small = F.attn_workspace_bytes(64, 32, 16, 4, 128, 16, 512, 4)

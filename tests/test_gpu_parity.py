@@ -203,13 +203,15 @@ def test_step_never_gathers_decoded_rows():
     st.hidden[dec] = sentinel
     st.q_att[dec] = sentinel
     ref = O.step(st)
-    fs, gpu = run_gpu_step(st)
-    excused = check_keep(gpu["keep"], ref["keep"], ref["delta"], st.masked, st.rule,
-                         gpu["kept_count"])
-    check_ragged(gpu, ref, st.B, excused, st.rule, gathered_sets(gpu, st, ref["keep"]))
-    assert not (gpu["hidden_rows"] == sentinel).all(axis=1).any()
-    assert not (gpu["q_rows"] == sentinel).all(axis=(1, 2)).any()
-    compare_attention(gpu, ref, st.B, excused)
+    for gather_q in (True, False):
+        fs, gpu = run_gpu_step(st, gather_q=gather_q)
+        excused = check_keep(gpu["keep"], ref["keep"], ref["delta"], st.masked, st.rule,
+                             gpu["kept_count"])
+        check_ragged(gpu, ref, st.B, excused, st.rule, gathered_sets(gpu, st, ref["keep"]))
+        assert not (gpu["hidden_rows"] == sentinel).all(axis=1).any()
+        if gather_q:
+            assert not (gpu["q_rows"] == sentinel).all(axis=(1, 2)).any()
+        compare_attention(gpu, ref, st.B, excused)
 
 
 @pytest.mark.parametrize("nsets", [1, 2])
@@ -365,6 +367,13 @@ def test_attn_isolated(case):
     oerr = np.abs(go - ref_out).max() if T else 0.0
     lerr = np.abs(gl - ref_lse).max() if T else 0.0
     assert oerr <= OUT_TOL and lerr <= LSE_TOL, (oerr, lerr)
+    # the same rows with the queries read in place at the kept positions: the same bits
+    pout, plse = F.ragged_paged_attn_pos(t.q_att, torch.from_numpy(c["kept_pos"]).to(DEV),
+                                         c["d_offsets"], t.k_cache, t.v_cache, t.page_table,
+                                         t.prefix_len, t.k_blk, t.v_blk, bound, st.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(pout[:T].view(torch.int16), out[:T].view(torch.int16))
+    assert torch.equal(plse[:T].view(torch.int32), lse[:T].view(torch.int32))
     print(f"T={T} out err {oerr:.2e} lse err {lerr:.2e}")
 
 
@@ -488,6 +497,40 @@ def test_attn_invalid_device_data_gives_nan_rows(max_kept):
             oerr = (out[rows].float() - ref[rows].float()).abs().max().item()
             lerr = (lse[rows] - ref_lse[rows]).abs().max().item()
             assert oerr <= OUT_TOL and lerr <= LSE_TOL, (r, oerr, lerr)
+
+
+@pytest.mark.parametrize("max_kept", [4, 12, 24])
+def test_attn_pos_invalid_position_gives_nan_rows(max_kept):
+    # queries read in place: a kept position outside the block reads no memory outside the
+    # query tensor and turns its row (with the rows computed together with it) into NaN; the
+    # other requests' rows keep their bits (the columns, and so the cuts, do not change)
+    _announce(f"attn_pos invalid kept position, max_kept={max_kept}")
+    st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=6))
+    keep = _random_keep(np.random.default_rng(11), st.B, st.blk, max_kept, empty_frac=0.0)
+    c = attn_case_inputs(st, keep)
+    t = step_inputs(st)
+    pos = torch.from_numpy(c["kept_pos"]).to(DEV)
+    args = (t.k_cache, t.v_cache, t.page_table, t.prefix_len, t.k_blk, t.v_blk, max_kept,
+            st.sm_scale)
+    ref, ref_lse = F.ragged_paged_attn_pos(t.q_att, pos, c["d_offsets"], *args)
+    off = c["offsets"]
+    bad_rows = {int(off[2]): st.blk + 5, int(off[5]) - 1: -1}  # requests 2 and 4
+    bpos = pos.clone()
+    for n, v in bad_rows.items():
+        bpos[n] = v
+    out, lse = F.ragged_paged_attn_pos(t.q_att, bpos, c["d_offsets"], *args)
+    torch.cuda.synchronize()
+    for n in bad_rows:
+        assert torch.isnan(out[n].float()).all() and torch.isnan(lse[n]).all(), n
+    for r in range(st.B):
+        for n in range(int(off[r]), int(off[r + 1])):
+            same = torch.equal(out[n].view(torch.int16), ref[n].view(torch.int16)) and \
+                torch.equal(lse[n].view(torch.int32), ref_lse[n].view(torch.int32))
+            if r in (2, 4):
+                assert same or (torch.isnan(out[n].float()).all() and
+                                torch.isnan(lse[n]).all()), (r, n)
+            else:
+                assert same, (r, n)
 
 
 def test_step_edge_cases_empty_prefix_and_nothing_masked():
@@ -948,21 +991,29 @@ def test_fused_step_equals_separate_calls(name, over):
     st = make_step(BY_NAME[name].scaled(**over))
     _announce(f"fused vs separate {name} {over}")
     from parity_helpers import fetch
-    fs = FocusStep(step_inputs(st))
-    fs.run_unfused()
-    torch.cuda.synchronize()
-    a = fetch(fs)
-    for nm in ("out", "delta", "q_rows", "hidden_rows", "keep", "kept_count", "offsets"):
-        t = getattr(fs, nm)
-        if t is not None:
-            t.fill_(0)
-    fs.run()
-    torch.cuda.synchronize()
-    b = fetch(fs)
-    for key in ("delta", "keep", "kept_count", "offsets", "kept_pos", "out_bits", "lse",
-                "hidden_rows"):
-        if key in a:
-            assert np.array_equal(a[key], b[key]), key
+    inp = step_inputs(st)
+    runs = []
+    for gather_q in (True, False):
+        fs = FocusStep(inp, gather_q=gather_q)
+        fs.run_unfused()
+        torch.cuda.synchronize()
+        a = fetch(fs)
+        for nm in ("out", "delta", "q_rows", "hidden_rows", "keep", "kept_count", "offsets"):
+            t = getattr(fs, nm)
+            if t is not None:
+                t.fill_(0)
+        fs.run()
+        torch.cuda.synchronize()
+        b = fetch(fs)
+        for key in ("delta", "keep", "kept_count", "offsets", "kept_pos", "out_bits", "lse",
+                    "hidden_rows", "q_rows"):
+            if key in a:
+                assert np.array_equal(a[key], b[key]), (gather_q, key)
+        runs.append(b)
+    # queries read in place give the bits of the attention over the gathered queries
+    for key in ("delta", "keep", "offsets", "kept_pos", "out_bits", "lse", "hidden_rows"):
+        if key in runs[0]:
+            assert np.array_equal(runs[0][key], runs[1][key]), key
 
 
 @pytest.mark.parametrize("name,over,cap_frac", [
