@@ -394,27 +394,47 @@ struct QOperand {
   }
 };
 
+// The kept positions of the cursor's query rows (one per query tile and lane; row rho is
+// token rho / G of the item), when the queries are read in place; issued ahead of the row loads
+// so that their round trip can overlap others (the page ids of the first tile).
+template <int QT>
+struct QPos {
+  int j[QT];
+};
+template <int QT>
+__device__ __forceinline__ QPos<QT> fetch_qpos(const Cursor& c, const Params& p, int lane) {
+  constexpr int R = 16 * QT;
+  QPos<QT> q;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    q.j[qt] = 0;
+    if (p.q_pos != nullptr) {  // wave-uniform
+      const int rho = min(c.qg * R + 16 * qt + (lane & 15), c.nrows - 1);
+      q.j[qt] = p.q_pos[min(c.off0 + (rho >> p.log2G), p.cap - 1)];
+    }
+  }
+  return q;
+}
+
 // Loads the Q operand of the cursor's item.  Rows past the item's rows (or past cap) are
 // clamped to a valid row: their results are never written, and finite inputs keep them finite.
-// With q_pos the rows are read where they are, at the kept positions of the request's block:
+// With q_pos the rows are read where they are, at the kept positions qp of the request's block:
 // a position outside the block reads position 0 and is reported (true: the item's rows become
 // NaN).
 template <int D, int QT>
-__device__ __forceinline__ bool load_q(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
-                                       int lane) {
+__device__ __forceinline__ bool load_q_at(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
+                                          int lane, const QPos<QT>& qp) {
   constexpr int NK = D / 32, R = 16 * QT;
   const int m16 = lane & 15, j4 = lane >> 4;
   bool bad = false;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int rho = min(c.qg * R + 16 * qt + m16, c.nrows - 1);
-    const int tok = min(c.off0 + (rho >> p.log2G), p.cap - 1);
-    int src = tok;
+    int src = min(c.off0 + (rho >> p.log2G), p.cap - 1);
     if (p.q_pos != nullptr) {  // wave-uniform
-      const int j = p.q_pos[tok];
-      const bool out = (unsigned)j >= (unsigned)p.blk;
+      const bool out = (unsigned)qp.j[qt] >= (unsigned)p.blk;
       bad = bad || out;
-      src = c.r * p.blk + (out ? 0 : j);
+      src = c.r * p.blk + (out ? 0 : qp.j[qt]);
     }
     const uint16_t* qrow =
         p.q + ((size_t)src * p.Hq + c.g * p.G + (rho & (p.G - 1))) * D + 8 * j4;
@@ -430,6 +450,12 @@ __device__ __forceinline__ bool load_q(QOperand<D, QT>& qf, const Cursor& c, con
     }
   }
   return bad;
+}
+
+template <int D, int QT>
+__device__ __forceinline__ bool load_q(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
+                                       int lane) {
+  return load_q_at<D, QT>(qf, c, p, lane, fetch_qpos<QT>(c, p, lane));
 }
 
 // Scores of one query tile from its Q^T fragments: S^T (32 keys x 16 rows) as two 16-key
@@ -1010,7 +1036,11 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
   QOperand<D, QT> qf;
   if constexpr (QOperand<D, QT>::kLds)
     qf.lds = reinterpret_cast<u32x4_t*>(s_q) + (size_t)wave * QT * NK * 64;
-  bool qbad = load_q<D, QT>(qf, C, p, lane);  // the current item's rows read a bad position
+  // the first piece's query positions and its first tile's page ids are requested together,
+  // then its query rows (a second round trip that overlaps the first tile's)
+  const QPos<QT> qp0 = fetch_qpos<QT>(C, p, lane);
+  const Pages pg0 = fetch_pages(C, p, page_table);
+  bool qbad = load_q_at<D, QT>(qf, C, p, lane, qp0);  // the current item's rows read a bad position
   Cursor L = C;
   int tvl = 0, tvc = 0;  // processing indices of L and C
   auto next = [&](Cursor& c, int& idx) {
@@ -1036,7 +1066,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       if (k > 0 && tvl + 1 < n) next(L, tvl);
-      const bool b = issue_share<D, WO>(L, fetch_pages(L, p, page_table), p, tid,
+      const bool b = issue_share<D, WO>(L, k == 0 ? pg0 : fetch_pages(L, p, page_table), p, tid,
                                         ring + (size_t)k * CH);
       badbits |= (b ? 1 : 0) << k;
     }
@@ -1093,7 +1123,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k) {
     if (k > 0 && tvl + 1 < n) next(L, tvl);
-    load_tile<D, WO>(tl[k], L, fetch_pages(L, p, page_table), p, lane);
+    load_tile<D, WO>(tl[k], L, k == 0 ? pg0 : fetch_pages(L, p, page_table), p, lane);
   }
   if (tvl + 1 < n) next(L, tvl);
   int tv = 0;
