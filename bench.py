@@ -300,15 +300,15 @@ def _counters_per_dispatch(root):
 
 def focused_attn_kernel(recipe):
     """Name of the attention instantiation the focused step of a recipe launches, as the launch
-    plan chooses it: <d, query tiles per wave, tiles in flight, output, shared tiles>.  Items of
-    33..128 rows share each tile among a workgroup's four waves (16 rows per wave up to 64, 32
-    rows with one share in flight above, three below); the others run one wave per item."""
+    plan chooses it: <d, query tiles per wave, tiles in flight, output, shared tiles, queries
+    read in place>.  Items of 33..128 rows share each tile among a workgroup's four waves (16
+    rows per wave up to 64, 32 rows above); the others run one wave per item."""
     rows = recipe.max_kept() * recipe.G
     if 32 < rows <= 128:
         qt = 1 if rows <= 64 else 2
-        return f"attn_kernel<{recipe.d}, {qt}, {3 if qt == 1 else 1}, true, true>"
+        return f"attn_kernel<{recipe.d}, {qt}, 3, true, true, true>"
     qt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
-    return f"attn_kernel<{recipe.d}, {qt}, 2, true, false>"
+    return f"attn_kernel<{recipe.d}, {qt}, 2, true, false, true>"
 
 
 def _kernel_table(csv_path, title, command):
@@ -783,7 +783,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "ragged paged attention (focus_ragged_paged_attn)",
+            "kernel": "ragged paged attention, queries read in place (focus_ragged_paged_attn_pos)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),

@@ -382,6 +382,7 @@ int attn_call(const void* q, const int32_t* q_pos, const int32_t* offsets, int c
   if (!offsets || !prefix_len || !k_blk || (!lse_only && !v_blk)) return FOCUS_ERR_INVALID_ARG;
   if (cap > 0 && (!q || (lse_only && !lse))) return FOCUS_ERR_INVALID_ARG;
   if (positional && cap > 0 && !q_pos) return FOCUS_ERR_INVALID_ARG;
+  if (positional && lse_only && cap > 0) return FOCUS_ERR_UNSUPPORTED;  // with the output only
   if (B <= 0 || blk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || S <= 0 || cap < 0 ||
       num_pages < 0 || max_pages < 0 || max_kept <= 0)
     return FOCUS_ERR_INVALID_ARG;

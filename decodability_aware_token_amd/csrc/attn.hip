@@ -395,20 +395,20 @@ struct QOperand {
 };
 
 // The kept positions of the cursor's query rows (one per query tile and lane; row rho is
-// token rho / G of the item), when the queries are read in place; issued ahead of the row loads
-// so that their round trip can overlap others (the page ids of the first tile).
+// token rho / G of the item), when the queries are read in place (POS); issued ahead of the
+// row loads so that their round trip can overlap others (the page ids of the first tile).
 template <int QT>
 struct QPos {
   int j[QT];
 };
-template <int QT>
+template <int QT, bool POS>
 __device__ __forceinline__ QPos<QT> fetch_qpos(const Cursor& c, const Params& p, int lane) {
   constexpr int R = 16 * QT;
   QPos<QT> q;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     q.j[qt] = 0;
-    if (p.q_pos != nullptr) {  // wave-uniform
+    if constexpr (POS) {
       const int rho = min(c.qg * R + 16 * qt + (lane & 15), c.nrows - 1);
       q.j[qt] = p.q_pos[min(c.off0 + (rho >> p.log2G), p.cap - 1)];
     }
@@ -418,10 +418,10 @@ __device__ __forceinline__ QPos<QT> fetch_qpos(const Cursor& c, const Params& p,
 
 // Loads the Q operand of the cursor's item.  Rows past the item's rows (or past cap) are
 // clamped to a valid row: their results are never written, and finite inputs keep them finite.
-// With q_pos the rows are read where they are, at the kept positions qp of the request's block:
-// a position outside the block reads position 0 and is reported (true: the item's rows become
-// NaN).
-template <int D, int QT>
+// POS: the rows are read where they are, at the kept positions qp of the request's block
+// (q is [B, blk, Hq, d]); a position outside the block reads position 0 and is reported (true:
+// the item's rows become NaN).  Otherwise q holds the compacted rows and qp is not used.
+template <int D, int QT, bool POS>
 __device__ __forceinline__ bool load_q_at(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
                                           int lane, const QPos<QT>& qp) {
   constexpr int NK = D / 32, R = 16 * QT;
@@ -431,7 +431,7 @@ __device__ __forceinline__ bool load_q_at(QOperand<D, QT>& qf, const Cursor& c, 
   for (int qt = 0; qt < QT; ++qt) {
     const int rho = min(c.qg * R + 16 * qt + m16, c.nrows - 1);
     int src = min(c.off0 + (rho >> p.log2G), p.cap - 1);
-    if (p.q_pos != nullptr) {  // wave-uniform
+    if constexpr (POS) {
       const bool out = (unsigned)qp.j[qt] >= (unsigned)p.blk;
       bad = bad || out;
       src = c.r * p.blk + (out ? 0 : qp.j[qt]);
@@ -452,10 +452,10 @@ __device__ __forceinline__ bool load_q_at(QOperand<D, QT>& qf, const Cursor& c, 
   return bad;
 }
 
-template <int D, int QT>
+template <int D, int QT, bool POS>
 __device__ __forceinline__ bool load_q(QOperand<D, QT>& qf, const Cursor& c, const Params& p,
                                        int lane) {
-  return load_q_at<D, QT>(qf, c, p, lane, fetch_qpos<QT>(c, p, lane));
+  return load_q_at<D, QT, POS>(qf, c, p, lane, fetch_qpos<QT, POS>(c, p, lane));
 }
 
 // Scores of one query tile from its Q^T fragments: S^T (32 keys x 16 rows) as two 16-key
@@ -652,7 +652,7 @@ __device__ __forceinline__ int slice_begin(int i, int total, int n) {
 // page_table is a separate restrict argument so that its (uniform) reads become scalar loads.
 // SH: shared tiles (the workgroup's four waves are four query groups of one kv head; NB is then
 // the number of tiles whose shares are in flight in registers).
-template <int D, int QT, int NB, bool WO, bool SH>
+template <int D, int QT, int NB, bool WO, bool SH, bool POS>
 __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
                                      : ((NB == 2 && QT == 1) ? 2 : 1)) void attn_kernel(
     Params p, const int32_t* __restrict__ page_table) {
@@ -1036,11 +1036,12 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
   QOperand<D, QT> qf;
   if constexpr (QOperand<D, QT>::kLds)
     qf.lds = reinterpret_cast<u32x4_t*>(s_q) + (size_t)wave * QT * NK * 64;
-  // the first piece's query positions and its first tile's page ids are requested together,
-  // then its query rows (a second round trip that overlaps the first tile's)
-  const QPos<QT> qp0 = fetch_qpos<QT>(C, p, lane);
-  const Pages pg0 = fetch_pages(C, p, page_table);
-  bool qbad = load_q_at<D, QT>(qf, C, p, lane, qp0);  // the current item's rows read a bad position
+  // POS: the first piece's query positions and its first tile's page ids are requested
+  // together, then its query rows (a second round trip that overlaps the first tile's)
+  const QPos<QT> qp0 = fetch_qpos<QT, POS>(C, p, lane);
+  Pages pg0{0, 0};
+  if constexpr (POS) pg0 = fetch_pages(C, p, page_table);
+  bool qbad = load_q_at<D, QT, POS>(qf, C, p, lane, qp0);  // the item's rows read a bad position
   Cursor L = C;
   int tvl = 0, tvc = 0;  // processing indices of L and C
   auto next = [&](Cursor& c, int& idx) {
@@ -1066,8 +1067,8 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       if (k > 0 && tvl + 1 < n) next(L, tvl);
-      const bool b = issue_share<D, WO>(L, k == 0 ? pg0 : fetch_pages(L, p, page_table), p, tid,
-                                        ring + (size_t)k * CH);
+      const bool b = issue_share<D, WO>(L, (POS && k == 0) ? pg0 : fetch_pages(L, p, page_table),
+                                        p, tid, ring + (size_t)k * CH);
       badbits |= (b ? 1 : 0) << k;
     }
     if (tvl + 1 < n) next(L, tvl);
@@ -1078,7 +1079,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
       if (live && tv > 0 && (C.tt == 0 || tv == n1)) {
         // a new piece's queries: the newest loads, so waiting for them waits for every tile
         // in flight too (the alternative, a wait at each use, would drain every step)
-        qbad = load_q<D, QT>(qf, C, p, lane);
+        qbad = load_q<D, QT, POS>(qf, C, p, lane);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1123,7 +1124,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
 #pragma unroll
   for (int k = 0; k < NB - 1; ++k) {
     if (k > 0 && tvl + 1 < n) next(L, tvl);
-    load_tile<D, WO>(tl[k], L, k == 0 ? pg0 : fetch_pages(L, p, page_table), p, lane);
+    load_tile<D, WO>(tl[k], L, (POS && k == 0) ? pg0 : fetch_pages(L, p, page_table), p, lane);
   }
   if (tvl + 1 < n) next(L, tvl);
   int tv = 0;
@@ -1134,7 +1135,7 @@ __global__ __launch_bounds__(256, SH ? (QT == 1 ? kShWgsPerCuQt1 : kShWgsPerCu)
   auto step = [&](Tile<D>& X, Tile<D>& Y) {
     const bool live = tv < n;
     const Pages pg = fetch_pages(L, p, page_table);
-    if (live && tv > 0 && (C.tt == 0 || tv == n1)) qbad = load_q<D, QT>(qf, C, p, lane);
+    if (live && tv > 0 && (C.tt == 0 || tv == n1)) qbad = load_q<D, QT, POS>(qf, C, p, lane);
     load_tile<D, WO>(Y, L, pg, p, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     if (live) {
@@ -1198,7 +1199,14 @@ size_t attn_lds_bytes(int B, int D, int QT, bool SH) {
 template <int D, int QT, bool WO, bool SH = false>
 hipError_t launch_dq(const Params& prm, const AttnPlan& plan, hipStream_t s) {
   constexpr int NB = prefetch_of(QT, SH);
-  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH>), dim3(plan.wgs), dim3(256),
+  if constexpr (WO) {
+    if (prm.q_pos != nullptr) {  // queries read in place (with the output only)
+      hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH, true>), dim3(plan.wgs), dim3(256),
+                         attn_lds_bytes(prm.B, D, QT, SH), s, prm, prm.page_table);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_kernel<D, QT, NB, WO, SH, false>), dim3(plan.wgs), dim3(256),
                      attn_lds_bytes(prm.B, D, QT, SH), s, prm, prm.page_table);
   return hipGetLastError();
 }

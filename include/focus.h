@@ -272,7 +272,8 @@ int focus_ragged_paged_attn(const void* q, const int32_t* offsets, int cap, cons
  * (offsets[r] <= n < offsets[r+1]) has the query q_block[r, kept_pos[n], h, :].
  *   q_block  [B, blk, Hq, d] bf16;  kept_pos [cap] i32 (as produced by focus_compact or the
  *            fused front ends)
- *   every other argument, layout, workspace and supported size as in call 4.
+ *   every other argument, layout, workspace and supported size as in call 4, except that out
+ *   is required (the log-sum-exp-only mode takes compacted queries: call 4).
  * Device data the host cannot check: a position outside [0, blk) gives NaN in all rows of its
  * request's kv-head group (as an invalid page id does) instead of a memory access.
  * ------------------------------------------------------------------------------------------ */

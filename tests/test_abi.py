@@ -249,6 +249,7 @@ def test_attn_pos_errors():
     assert ap(q=P + 8) == F.FOCUS_ERR_INVALID_ARG               # misaligned
     assert ap(S=48) == F.FOCUS_ERR_UNSUPPORTED                  # as call 4
     assert ap(ws=None, maxp=128) == F.FOCUS_ERR_WORKSPACE
+    assert ap(out=None) == F.FOCUS_ERR_UNSUPPORTED              # log-sum-exp only: call 4
     assert ap(cap=0, q=None, pos=None, out=None) == F.FOCUS_OK  # nothing kept: nothing launched
 
 

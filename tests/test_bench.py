@@ -54,7 +54,7 @@ def _write_pmc(path, counter, rows):
 
 def test_profile_summary_scales_counters_by_the_copy(tmp_path, monkeypatch):
     out = tmp_path / "out"
-    attn = ("void focus::(anonymous namespace)::attn_kernel<128, 1, 2, true, false>"
+    attn = ("void focus::(anonymous namespace)::attn_kernel<128, 1, 2, true, false, true>"
             "(focus::Params, int const*)")
     copy = "__amd_rocclr_copyBuffer(void*)"
     w = out / "sdar_b256_blk32"
@@ -80,7 +80,7 @@ def test_profile_summary_scales_counters_by_the_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
     bench.summarize_profiles(str(out), "sdar_b256_blk32")
     rec = json.load(open(tmp_path / "profiles" / "attn_traffic_sdar_b256_blk32.json"))
-    assert rec["kernel"] == "attn_kernel<128, 1, 2, true, false>"
+    assert rec["kernel"] == "attn_kernel<128, 1, 2, true, false, true>"
     assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
     assert rec["hbm_read_bytes"] == 2000 * 1024 * 2
     assert rec["hbm_write_bytes"] == 10 * 1024
@@ -88,18 +88,19 @@ def test_profile_summary_scales_counters_by_the_copy(tmp_path, monkeypatch):
     assert rec["mfma_bf16_flops_per_launch"] == 2.0e6 * 512
     assert rec["trace_avg_us"] == 150.0
     table = open(tmp_path / "profiles" / "kernels_sdar_b256_blk32.txt").read()
-    assert "attn_kernel<128, 1, 2, true, false>" in table and "150.00" in table
+    assert "attn_kernel<128, 1, 2, true, false, true>" in table and "150.00" in table
 
 
 def test_focused_attention_instantiation_per_recipe():
     from workloads import BY_NAME
-    one_wave = {"sdar_b256_blk32": "attn_kernel<128, 1, 2, true, false>",
-                "sdar_b32_blk32": "attn_kernel<128, 2, 2, true, false>",
-                "longctx_b64_blk32": "attn_kernel<128, 1, 2, true, false>",
-                "tiny_b2_blk16": "attn_kernel<64, 1, 2, true, false>"}
+    # the focused step reads its queries in place (the last template argument)
+    one_wave = {"sdar_b256_blk32": "attn_kernel<128, 1, 2, true, false, true>",
+                "sdar_b32_blk32": "attn_kernel<128, 2, 2, true, false, true>",
+                "longctx_b64_blk32": "attn_kernel<128, 1, 2, true, false, true>",
+                "tiny_b2_blk16": "attn_kernel<64, 1, 2, true, false, true>"}
     # the adaptive recipes' launch bound is 16 kept tokens x 4 query heads = 64 rows: shared
-    shared = {"sweep_b128_blk64": "attn_kernel<128, 1, 3, true, true>",
-              "sweep_b128_blk16": "attn_kernel<128, 1, 3, true, true>"}
+    shared = {"sweep_b128_blk64": "attn_kernel<128, 1, 3, true, true, true>",
+              "sweep_b128_blk16": "attn_kernel<128, 1, 3, true, true, true>"}
     for name, want in {**one_wave, **shared}.items():
         assert bench.focused_attn_kernel(BY_NAME[name]) == want, name
 
