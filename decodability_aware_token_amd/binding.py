@@ -256,6 +256,9 @@ def ragged_paged_attn_pos(q_block, kept_pos, offsets, k_cache, v_cache, page_tab
     num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
     S = k_cache.shape[3]
     max_pages = page_table.shape[1]
+    if page_table.shape[0] != B or prefix_len.shape[0] != B or k_blk.shape[0] != B or \
+            k_blk.shape[3] != blk:
+        raise ValueError("q_block, page_table, prefix_len and k_blk disagree on B or blk")
     dev = q_block.device
     if out is None:
         out = torch.empty((cap, Hq, d), dtype=torch.bfloat16, device=dev)
@@ -296,10 +299,17 @@ def kv_pack(k_src=None, v_src=None, token_major: bool = False, k_out=None, v_out
     S, Hkv = (src.shape[1], src.shape[2]) if token_major else (src.shape[2], src.shape[1])
     d = src.shape[3]
     dev = src.device
+    for x in (k_src, v_src):
+        if x is not None and tuple(x.shape) != tuple(src.shape):
+            raise ValueError("k_src and v_src must have the same shape")
     if k_src is not None and k_out is None:
         k_out = torch.empty((n, Hkv, d // 8, S, 8), dtype=torch.bfloat16, device=dev)
     if v_src is not None and v_out is None:
         v_out = torch.empty((n, Hkv, S // 8, d, 8), dtype=torch.bfloat16, device=dev)
+    if k_src is not None and k_out.numel() != src.numel():
+        raise ValueError("k_out must hold n * Hkv * S * d elements")
+    if v_src is not None and v_out.numel() != src.numel():
+        raise ValueError("v_out must hold n * Hkv * S * d elements")
     layout = FOCUS_KV_TOKEN_MAJOR if token_major else FOCUS_KV_HEAD_MAJOR
     rc = lib().focus_kv_pack(_ptr(k_src) if k_src is not None else None,
                              _ptr(v_src) if v_src is not None else None, layout, n, Hkv, S, d,
