@@ -41,6 +41,9 @@
 // ring of four LDS tile buffers, three tiles ahead, one barrier per tile), and each wave reads
 // the MFMA fragments above from LDS -- the keys, then, after its scores, the values into the
 // same registers.
+// Queries.  Either compacted rows [cap, Hq, d] (row n is the n-th kept token), or, in the POS
+// instantiations, the block's query tensor [B, blk, Hq, d] read in place at the kept positions
+// (row n of request r is q[r, q_pos[n]]): the same operands, without a gather beforehand.
 // Softmax is online in the exp2 domain (f32).  Merges run in a fixed order, so results are
 // bitwise reproducible.
 #include <algorithm>
