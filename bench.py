@@ -298,6 +298,10 @@ def _counters_per_dispatch(root):
     return vals
 
 
+FRONT_KERNELS = ("score_partial_kernel", "score_reduce_kernel", "select_compact_kernel",
+                 "select_kernel", "compact_kernel", "compact_scan_kernel")
+
+
 def focused_attn_kernel(recipe):
     """Name of the attention instantiation the focused step of a recipe launches, as the launch
     plan chooses it: <d, query tiles per wave, tiles in flight, output, shared tiles, queries
@@ -397,7 +401,22 @@ def summarize_profiles(out_root, workload):
         txt.append(f"kernel-trace average duration {avg[key]:.2f} us")
     with open(os.path.join(prof, f"attn_traffic_{workload}.txt"), "w") as fh:
         fh.write("\n".join(txt) + "\n")
-    print("\n".join(lines + txt))
+    # the front end's kernels from the same counter runs (every kernel of the step is counted)
+    allf = _counters_per_dispatch(os.path.join(w, "fetch"))
+    allw = _counters_per_dispatch(os.path.join(w, "write"))
+    front = [f"# HBM traffic of the front-end kernels, workload {workload} (focused step; the "
+             "same counter runs, scaled by the copy calibration)",
+             *[f"# command: {c}" for c in rec["commands"][:4]],
+             f"{'kernel':56s} {'read MB':>9s} {'written MB':>11s} {'trace avg us':>13s}"]
+    for name in sorted(allf):
+        if not name.startswith(FRONT_KERNELS):
+            continue
+        r_mb = med(allf[name]["FETCH_SIZE"]) * 1024.0 * f_fac / 1e6
+        w_mb = med(allw.get(name, {}).get("WRITE_SIZE", [0.0])) * 1024.0 * w_fac / 1e6
+        front.append(f"{name[:56]:56s} {r_mb:9.2f} {w_mb:11.2f} {avg.get(name, float('nan')):13.2f}")
+    with open(os.path.join(prof, f"front_traffic_{workload}.txt"), "w") as fh:
+        fh.write("\n".join(front) + "\n")
+    print("\n".join(lines + txt + front))
 
 
 class Flush:

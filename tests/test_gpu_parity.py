@@ -533,6 +533,29 @@ def test_attn_pos_invalid_position_gives_nan_rows(max_kept):
                 assert same, (r, n)
 
 
+@pytest.mark.parametrize("max_kept", [4, 12])
+def test_attn_pos_capacity_cut(max_kept):
+    # a capacity below the kept rows: the in-place call reads positions and writes rows only
+    # below cap, with the bits of the compacted call under the same cap
+    _announce(f"attn_pos capacity cut, max_kept={max_kept}")
+    st = make_step(BY_NAME["sdar_b32_blk32"].scaled(B=8))
+    keep = _random_keep(np.random.default_rng(13), st.B, st.blk, max_kept, empty_frac=0.0)
+    c = attn_case_inputs(st, keep)
+    t = step_inputs(st)
+    T = int(c["offsets"][-1])
+    cap = T - 7
+    args = (t.k_cache, t.v_cache, t.page_table, t.prefix_len, t.k_blk, t.v_blk, max_kept,
+            st.sm_scale)
+    ref, ref_lse = F.ragged_paged_attn(c["d_q"][:cap].contiguous(), c["d_offsets"], *args)
+    sentinel = torch.full((T, st.Hq, st.d), 7.0, dtype=torch.bfloat16, device=DEV)
+    pos = torch.from_numpy(c["kept_pos"][:cap].copy()).to(DEV)
+    out, lse = F.ragged_paged_attn_pos(t.q_att, pos, c["d_offsets"], *args, out=sentinel[:cap])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+    assert torch.all(sentinel[cap:] == 7.0)
+
+
 def test_step_edge_cases_empty_prefix_and_nothing_masked():
     _announce("step edge cases")
     rec = BY_NAME["sdar_b32_blk32"].scaled(B=6, prefix=("uniform", 0, 200), budget=("fixed", 3))
