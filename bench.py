@@ -605,6 +605,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdar_b256_blk32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the workload's recipe at this batch size instead (a batch-scaling "
+                         "point, named <workload>_b<B>; no counter record applies to it)")
     ap.add_argument("--no-full-domain", action="store_true",
                     help="skip the full-domain importance measurement")
     ap.add_argument("--no-full-block", action="store_true",
@@ -673,6 +676,8 @@ def main():
     from workloads.torch_io import upload
 
     recipe = BY_NAME[args.workload]
+    if args.batch:  # the workload's recipe at another batch size (same seed and distributions)
+        recipe = recipe.scaled(B=args.batch, name=f"{recipe.name}_b{args.batch}")
     only = args.only_step
     log(f"[bench] generating {recipe.name}")
     st = make_step(recipe, layer0_prefix=not (args.no_full_domain or only))
